@@ -1,0 +1,174 @@
+"""Seeded synthetic inputs for the quantized-linear workloads.
+
+This module only draws inputs; it holds none of the arithmetic of the
+quantized linear layer (no quantization, no GEMM, no repack). Both the test
+suite and the benchmark draw their inputs from here, so the GPU path and the
+CPU oracle always see identical bytes.
+
+Workload shapes and distributions:
+
+* QAT grid weights ("Gemma 4 ... QAT q4_0 unquantized" release, as described
+  in the MI300X article, section "Ten builds", and the 31B model card): every
+  Linear weight lies on a 4-bit grid with one scale per 32 consecutive values
+  along K, stored as bf16. Synthetic stand-in: codes uniform in [-8, 7], one
+  fp32 step per (output row, group of 32) drawn lognormal(ln 0.01, 0.5) and
+  rounded to the nearest bf16 (so the stored bf16 tensor determines the step
+  exactly), materialised as bf16(code * step).
+* Activations: bf16 N(0, 1) with 1 % of entries multiplied by 20 (outliers),
+  drawn once at the largest M of a configuration; smaller M use leading rows.
+* MoE routing (router outside the block): N(0, 1) fp32 router logits, top-8
+  of the softmax, weights not renormalised. Ties go to the lower expert id.
+
+Draw order inside one configuration: weights (per matrix codes, then steps;
+for the MoE experts in ascending order, gate_up then down), then activations,
+then router logits.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 32
+
+
+# --------------------------------------------------------------------------
+# bf16 storage helpers (input materialisation only)
+# --------------------------------------------------------------------------
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# element generators
+# --------------------------------------------------------------------------
+def qat_grid(rng: np.random.Generator, n: int, k: int):
+    """One Linear weight on the QAT q4_0 grid.
+
+    Returns (codes int8 [n,k] in [-8,7], steps float32 [n,k/32] holding bf16
+    values, w_bf16 uint16 [n,k] = bf16(code*step)).
+    """
+    assert k % GROUP == 0
+    codes = rng.integers(-8, 8, size=(n, k), dtype=np.int8)
+    steps = rng.lognormal(np.log(0.01), 0.5, size=(n, k // GROUP)).astype(np.float32)
+    steps = bf16_bits_to_f32(to_bf16_bits(steps))
+    w = codes.astype(np.float32).reshape(n, k // GROUP, GROUP) * steps[:, :, None]
+    w_bf16 = to_bf16_bits(w.reshape(n, k))
+    return codes, steps, w_bf16
+
+
+def activations(rng: np.random.Generator, m: int, k: int) -> np.ndarray:
+    """bf16 bits [m,k]: N(0,1) with 1 % of entries scaled by 20."""
+    x = rng.standard_normal(size=(m, k), dtype=np.float32)
+    mask = rng.random(size=(m, k), dtype=np.float32) < 0.01
+    x[mask] *= 20.0
+    return to_bf16_bits(x)
+
+
+def route_topk(logits: np.ndarray, topk: int):
+    """Router stand-in: softmax over experts, top-k ids and probabilities.
+
+    The router sits outside the MoE block; its output is an input of the
+    block. Returns (ids int32 [T,topk], probs float32 [T,topk]).
+    """
+    lg = logits.astype(np.float64)
+    p = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    # stable sort on -p: equal probabilities keep ascending expert order
+    order = np.argsort(-p, axis=1, kind="stable")[:, :topk]
+    ids = order.astype(np.int32)
+    probs = np.take_along_axis(p, order, axis=1).astype(np.float32)
+    return ids, probs
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+CONFIGS = {
+    1: dict(name="C1 single layer M=4 K=256 N=512", seed=0, K=256, N=512, M=(4,)),
+    2: dict(name="C2 decode K=2048 N=8192", seed=1, K=2048, N=8192, M=(1, 8, 64)),
+    3: dict(name="C3 large decode K=5120 N=25600", seed=2, K=5120, N=25600, M=(1, 8, 64)),
+    4: dict(name="C4 prefill M=8192", seed=3, M=8192, shapes=((4096, 14336), (14336, 4096))),
+    5: dict(name="C5 MoE E=128 H=2048 I=768 top-8", seed=4, E=128, H=2048, I=768, topk=8,
+            T=(64, 512)),
+}
+
+
+def linear_config(cfg: int, n: int | None = None, k: int | None = None, m: int | None = None):
+    """Inputs of a dense configuration (1, 2 or 3).
+
+    Optional n/k/m override the sizes (same seed and draw order), for small
+    parity cases of the same distribution.
+    """
+    c = CONFIGS[cfg]
+    rng = np.random.default_rng(c["seed"])
+    N = c["N"] if n is None else n
+    K = c["K"] if k is None else k
+    M = max(c["M"]) if m is None else m
+    codes, steps, w_bf16 = qat_grid(rng, N, K)
+    a = activations(rng, M, K)
+    return dict(codes=codes, steps=steps, w_bf16=w_bf16, a=a, M=M, N=N, K=K)
+
+
+def prefill_config(which: int, m: int | None = None, rows_n: int | None = None):
+    """Inputs of configuration 4, shape index 0 (K=4096,N=14336) or 1.
+
+    Weights for both shapes are drawn first, then both activations, so the
+    draw order is fixed whichever shape is asked for. `m` / `rows_n` keep
+    only the leading rows (same bytes as the full draw).
+    """
+    c = CONFIGS[4]
+    rng = np.random.default_rng(c["seed"])
+    ws = [qat_grid(rng, n, k) for (k, n) in c["shapes"]]
+    acts = []
+    for (k, _n) in c["shapes"]:
+        acts.append(activations(rng, c["M"], k))
+    K, N = c["shapes"][which]
+    codes, steps, w_bf16 = ws[which]
+    a = acts[which]
+    if m is not None:
+        a = a[:m]
+    if rows_n is not None:
+        codes, steps, w_bf16 = codes[:rows_n], steps[:rows_n], w_bf16[:rows_n]
+        N = rows_n
+    return dict(codes=codes, steps=steps, w_bf16=w_bf16, a=np.ascontiguousarray(a),
+                M=a.shape[0], N=N, K=K)
+
+
+def moe_config(E: int | None = None, H: int | None = None, I: int | None = None,
+               T: int | None = None, topk: int | None = None, seed: int | None = None):
+    """Inputs of configuration 5 (or a smaller block of the same recipe).
+
+    Returns q4 grids of every expert: gate_up [E, 2I, H] and down [E, H, I]
+    (codes, steps, bf16), activations x [T,H] and routing ids/probs [T,topk].
+    """
+    c = CONFIGS[5]
+    E = c["E"] if E is None else E
+    H = c["H"] if H is None else H
+    I = c["I"] if I is None else I
+    T = max(c["T"]) if T is None else T
+    topk = c["topk"] if topk is None else topk
+    rng = np.random.default_rng(c["seed"] if seed is None else seed)
+    c13 = np.empty((E, 2 * I, H), np.int8)
+    s13 = np.empty((E, 2 * I, H // GROUP), np.float32)
+    w13 = np.empty((E, 2 * I, H), np.uint16)
+    c2 = np.empty((E, H, I), np.int8)
+    s2 = np.empty((E, H, I // GROUP), np.float32)
+    w2 = np.empty((E, H, I), np.uint16)
+    for e in range(E):
+        c13[e], s13[e], w13[e] = qat_grid(rng, 2 * I, H)
+        c2[e], s2[e], w2[e] = qat_grid(rng, H, I)
+    x = activations(rng, T, H)
+    logits = rng.standard_normal(size=(T, E), dtype=np.float32)
+    ids, probs = route_topk(logits, topk)
+    return dict(E=E, H=H, I=I, T=T, topk=topk, codes13=c13, steps13=s13, w13_bf16=w13,
+                codes2=c2, steps2=s2, w2_bf16=w2, x=x, logits=logits, ids=ids, probs=probs)
+

@@ -1,0 +1,196 @@
+"""Pins for the oracle's offline repacks (CPU only).
+
+* q4_0 repack: the generator's codes and steps are ground truth; the repack
+  must recover them exactly (MI300X Gemma 4 E2B article, "Step 1": the 4-bit
+  repack recovers each group's trained step and stores int4 without
+  re-rounding). Constructed groups exercise the counted cases.
+* FP8 per-channel repack: the pages print max error / row max = 8/240 for
+  E4M3FNUZ (E2B verify report) and 3.57 % = 16/448 for OCP E4M3 (31B model
+  card), which are the half-spacing of the top binade over the row max;
+  relative RMS 2.64 % on real weights. Brute force on small rows.
+* int8 per-channel: 255 levels per row (E2B article, fidelity section).
+* E4M3FNUZ -> OCP: all 256 codes, both branches.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import gen
+
+OCP, FNUZ, INT8 = 0, 1, 2
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_fidelity.json")))
+
+
+def _bf16(x):
+    return gen.to_bf16_bits(np.float32(x))
+
+
+@pytest.fixture(scope="module")
+def c2(oracle):
+    d = gen.linear_config(2)
+    p, s, amb = oracle.repack_q4_0(d["w_bf16"])
+    d.update(packed=p, steps_bits=s, amb=amb)
+    return d
+
+
+def test_q4_repack_recovers_generator_grid(oracle):
+    for cfg, kw in ((1, {}), (3, dict(n=64)), (2, dict(n=96, k=512))):
+        d = gen.linear_config(cfg, **kw)
+        p, s, amb = oracle.repack_q4_0(d["w_bf16"])
+        assert amb == 0
+        assert np.array_equal(oracle.unpack_q4(p, d["K"]), d["codes"])
+        assert np.array_equal(gen.bf16_bits_to_f32(s), d["steps"])
+        assert oracle.frac_bit_identical(p, s, d["w_bf16"]) == 1.0
+
+
+def test_q4_pack_layout(oracle):
+    # one row, codes -8..7 twice: low nibble holds the even k, u = c + 8
+    codes = np.tile(np.arange(-8, 8, dtype=np.int8), 2)[None, :]
+    w = gen.to_bf16_bits(codes.astype(np.float32) * np.float32(0.5))
+    p, s, amb = oracle.repack_q4_0(w)
+    assert amb == 0 and gen.bf16_bits_to_f32(s)[0, 0] == 0.5
+    u = codes[0].astype(np.int16) + 8
+    assert np.array_equal(p[0], (u[0::2] | (u[1::2] << 4)).astype(np.uint8))
+
+
+def _group(codes, step):
+    return gen.to_bf16_bits(np.asarray(codes, np.float32) * np.float32(step))[None, :]
+
+
+def test_q4_counted_cases(oracle):
+    step = float(gen.bf16_bits_to_f32(_bf16([0.0123]))[0])
+    rng = np.random.default_rng(11)
+    # (a) all-zero group: step 0, codes 0, counted
+    p, s, amb = oracle.repack_q4_0(np.zeros((1, 32), np.uint16))
+    assert amb == 1 and s[0, 0] == 0 and np.all(oracle.unpack_q4(p, 32) == 0)
+    # (b) no power-of-two code: recovered by the neighbour search, counted
+    c = rng.choice([-7, -6, -5, -3, 0, 3, 5, 6, 7], 32).astype(np.int8)
+    c[0] = 7
+    p, s, amb = oracle.repack_q4_0(_group(c, step))
+    assert amb == 1
+    assert np.array_equal(oracle.unpack_q4(p, 32)[0], c)
+    assert gen.bf16_bits_to_f32(s)[0, 0] == step
+    # (c) every code even and small: steps s/2, s and 2s all reproduce the
+    # values; the smallest (finest grid) is kept and the group is counted
+    c = rng.choice([-4, -2, 0, 2], 32).astype(np.int8)
+    c[:3] = [-4, 2, -2]
+    p, s, amb = oracle.repack_q4_0(_group(c, step))
+    assert amb == 1
+    assert gen.bf16_bits_to_f32(s)[0, 0] == step / 2
+    assert np.array_equal(oracle.unpack_q4(p, 32)[0], 2 * c)
+    # (d) values on no 4-bit grid: nearest codes on bf16(amax/7), counted
+    w = gen.to_bf16_bits(rng.standard_normal(32).astype(np.float32))[None, :]
+    p, s, amb = oracle.repack_q4_0(w)
+    assert amb == 1
+    st = gen.bf16_bits_to_f32(s)[0, 0]
+    wv = gen.bf16_bits_to_f32(w)[0]
+    amax = np.abs(wv).max()
+    assert st == gen.bf16_bits_to_f32(gen.to_bf16_bits(np.float32(amax) / np.float32(7)))
+    assert np.array_equal(oracle.unpack_q4(p, 32)[0],
+                          np.clip(np.rint(wv / st), -8, 7).astype(np.int8))
+
+
+def _grid(d):
+    return d["codes"].astype(np.float64) * np.repeat(d["steps"], 32, axis=1)
+
+
+@pytest.mark.parametrize("fmt", [OCP, FNUZ])
+def test_fp8_repack_matches_pages_fidelity(oracle, c2, fmt):
+    wq, ws = oracle.repack_fp8(c2["packed"], c2["steps_bits"], c2["K"], fmt)
+    rr, mr = oracle.repack_stats(c2["packed"], c2["steps_bits"], wq, ws, c2["K"], fmt)
+    if fmt == FNUZ:
+        page = GOLD["e2b_fnuz_verify_report"]
+        # max error / row max is 8/240 plus fp32 slack of the scale; the page's
+        # number has the same form
+        assert abs(mr - page["max_rel_err"]) < 1e-6
+        assert mr <= 1 / 30 + 1e-6
+        assert abs(rr - page["relative_rms_error"]) < 0.003
+    else:
+        card = GOLD["31b_ocp_model_card"]
+        assert round(mr * 100, 2) == card["largest_error_over_row_max_percent"]
+        assert mr <= 1 / 28 + 1e-6
+        assert abs(rr * 100 - card["relative_rms_error_percent"]) < 0.3
+
+
+@pytest.mark.parametrize("fmt", [OCP, FNUZ])
+def test_fp8_repack_bruteforce_rows(oracle, c2, fmt):
+    K = c2["K"]
+    rows = slice(0, 6)
+    wq, ws = oracle.repack_fp8(c2["packed"][rows], c2["steps_bits"][rows], K, fmt)
+    table = oracle.fp8_decode_table(fmt)
+    top = 0x7E if fmt == OCP else 0x7F
+    mags = table[: top + 1]
+    w = _grid(c2)[rows].astype(np.float32)  # exact
+    for n in range(w.shape[0]):
+        amax = np.abs(w[n]).max()
+        s = np.float32(amax) / np.float32(448.0 if fmt == OCP else 240.0)
+        assert ws[n] == s
+        v = np.abs(w[n] / s).astype(np.float64)
+        d = np.abs(mags[None, :] - v[:, None])
+        for k in range(K):
+            best = np.flatnonzero(d[k] == d[k].min())
+            c = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+            neg = w[n, k] < 0 or (w[n, k] == 0 and np.signbit(w[n, k]))
+            want = 0 if c == 0 and not (neg and fmt == OCP) else (c | (0x80 if neg else 0))
+            if c == 0 and neg and fmt == OCP:
+                want = 0x80
+            assert wq[n, k] == want, (n, k)
+        assert (wq[n] & 0x7F).max() == top  # the row max lands on the largest code
+
+
+def test_int8_repack(oracle, c2):
+    K = c2["K"]
+    wq, ws = oracle.repack_int8(c2["packed"], c2["steps_bits"], K)
+    assert wq.min() >= -127 and wq.max() <= 127
+    assert np.all(np.abs(wq.astype(np.int32)).max(axis=1) == 127)  # 255 levels, reached
+    w = _grid(c2).astype(np.float32)
+    s = np.abs(w).max(axis=1) / np.float32(127)
+    assert np.array_equal(ws, s.astype(np.float32))
+    ref = np.clip(np.rint(w[:8] / s[:8, None]), -127, 127).astype(np.int8)
+    assert np.array_equal(wq[:8], ref)
+    err = np.abs(wq.astype(np.float64) * ws[:, None] - w.astype(np.float64))
+    # half a level, plus the fp32 rounding of w / s (|w/s| <= 127)
+    assert np.all(err <= 0.5 * ws[:, None] * (1 + 127 * 2.0 ** -23))
+    rr, mr = oracle.repack_stats(c2["packed"], c2["steps_bits"], wq, ws, K, INT8)
+    assert rr < 0.015 and mr <= 0.5 / 127 + 1e-7
+
+
+def test_fnuz_to_ocp_enumeration(oracle):
+    tf = oracle.fp8_decode_table(FNUZ)
+    to = oracle.fp8_decode_table(OCP)
+    codes = np.array([b for b in range(256) if b != 0x80], np.uint8)
+    # branch A: no +-240 in the row -> identical bits, halved scale
+    a = codes[(codes & 0x7F) != 0x7F][None, :]
+    wo, so, bad = oracle.fnuz_to_ocp(a, np.float32([0.75]))
+    assert bad == 0 and np.array_equal(wo, a) and so[0] == np.float32(0.375)
+    assert np.array_equal(to[wo[0]] * so[0], tf[a[0]] * 0.75)
+    # branch B: row holds +-240 -> same scale, values re-encoded; odd
+    # mantissas in the two lowest binades (8 per sign) are not representable
+    wo, so, bad = oracle.fnuz_to_ocp(codes[None, :], np.float32([0.75]))
+    assert so[0] == np.float32(0.75)
+    e = (codes >> 3) & 15
+    m = codes & 7
+    inexact = (e <= 1) & (m % 2 == 1)
+    assert bad == int(inexact.sum()) == 16
+    vo, vi = to[wo[0]], tf[codes]
+    assert np.array_equal(vo[~inexact], vi[~inexact])
+    # inexact ones are the nearest-even OCP code of the value
+    for b, o in zip(codes[inexact], wo[0][inexact]):
+        assert o == oracle.fp8_encode(float(tf[b]), OCP)
+    # the invalid FNUZ code is counted
+    _, _, bad = oracle.fnuz_to_ocp(np.uint8([[0x80, 0x10]]), np.float32([1.0]))
+    assert bad == 1
+
+
+def test_fnuz_repack_converts_exactly(oracle, c2):
+    rows = slice(0, 512)
+    K = c2["K"]
+    wf, sf = oracle.repack_fp8(c2["packed"][rows], c2["steps_bits"][rows], K, FNUZ)
+    wo, so, bad = oracle.fnuz_to_ocp(wf, sf)
+    assert bad == 0
+    tf, to = oracle.fp8_decode_table(FNUZ), oracle.fp8_decode_table(OCP)
+    assert np.array_equal(to[wo] * so[:, None].astype(np.float64),
+                          tf[wf] * sf[:, None].astype(np.float64))
