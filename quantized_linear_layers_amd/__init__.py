@@ -1,0 +1,354 @@
+"""qlin: quantized linear layers for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libqlin.so`` (``include/qlin.h``).
+Every computation runs in the library's HIP kernels; this module only checks
+tensors, allocates outputs with torch and passes raw device pointers plus
+the current HIP stream. Importing it fails loudly if the library has not been
+built (``python quantized_linear_layers_amd/build.py``).
+
+bf16 tensors are ``torch.bfloat16``; FP8 codes are ``torch.uint8`` holding
+OCP E4M3 (or E4M3FNUZ) bit patterns; int8 codes are ``torch.int8``; int4
+codes are ``torch.uint8`` [N, K/2] (low nibble = even k, value c + 8).
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlin.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libqlin.so not found at {LIB_PATH}: build it with "
+        "`python quantized_linear_layers_amd/build.py` (hipcc, gfx950)")
+
+_lib = C.CDLL(LIB_PATH)
+
+# ---------------------------------------------------------------- constants
+OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = range(7)
+E4M3, E4M3FNUZ, INT8 = 0, 1, 2
+OUT_BF16, OUT_F32 = 0, 1
+OP_GEMM_FP8, OP_GEMM_W8A8, OP_GEMM_W4A16, OP_LINEAR_FP8, OP_LINEAR_W8A8 = range(5)
+
+_P, _I64, _INT, _SZ = C.c_void_p, C.c_int64, C.c_int, C.c_size_t
+_SIGS = {
+    "qlin_abi_version": (_INT, []),
+    "qlin_status_str": (C.c_char_p, [_INT]),
+    "qlin_last_hip_error": (_INT, []),
+    "qlin_repack_q4_0": (_INT, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "qlin_repack_fp8": (_INT, [_P, _P, _I64, _I64, _INT, _P, _P, _P]),
+    "qlin_repack_int8": (_INT, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "qlin_fp8_fnuz_to_ocp": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "qlin_dequant_q4_bf16": (_INT, [_P, _P, _I64, _I64, _P, _P]),
+    "qlin_quant_act": (_INT, [_P, _I64, _I64, _I64, _INT, _P, _P, _P]),
+    "qlin_fp8_encode_f32": (_INT, [_P, _I64, _INT, _P, _P]),
+    "qlin_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
+    "qlin_workspace_init": (_INT, [_P, _SZ, _P]),
+    "qlin_gemm_fp8": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _P, _SZ, _P]),
+    "qlin_gemm_w8a8": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _INT, _P, _SZ, _P]),
+    "qlin_gemm_w4a16": (_INT, [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _INT, _P, _SZ, _P]),
+    "qlin_linear_fp8": (_INT, [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "qlin_linear_w8a8": (_INT, [_P, _I64, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "qlin_moe_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
+    "qlin_moe_workspace_layout": (_INT, [_I64, _I64, _I64, _I64, _INT, C.POINTER(_SZ)]),
+    "qlin_moe_fp8": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _SZ, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class QlinError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.qlin_status_str(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {_lib.qlin_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The raw ctypes handle of libqlin.so."""
+    return _lib
+
+
+def _call(name: str, *args):
+    st = getattr(_lib, name)(*args)
+    if st != OK:
+        raise QlinError(name, st)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, ndim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_FMT = {"e4m3": E4M3, "e4m3fnuz": E4M3FNUZ, "int8": INT8, E4M3: E4M3, E4M3FNUZ: E4M3FNUZ,
+        INT8: INT8}
+
+# ---------------------------------------------------------------- workspace
+_ws_cache: dict[int, torch.Tensor] = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """Zero-initialised per-device workspace of at least nbytes (kept for
+    reuse; the library leaves its counter area zero after every call)."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _ws_cache.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[idx] = ws
+    return ws
+
+
+def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
+    return int(_lib.qlin_workspace_bytes(op, M, N, K))
+
+
+# ---------------------------------------------------------------- repacks
+def repack_q4_0(w: torch.Tensor):
+    """bf16 QAT weight [N,K] -> (codes u8 [N,K/2], steps bf16 [N,K/32],
+    n_ambiguous int64 [1] on device)."""
+    _check(w, "w", torch.bfloat16, 2)
+    N, K = w.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    steps = torch.empty((N, K // 32), dtype=torch.bfloat16, device=w.device)
+    amb = torch.empty(1, dtype=torch.int64, device=w.device)
+    _call("qlin_repack_q4_0", _ptr(w), N, K, _ptr(codes), _ptr(steps), _ptr(amb), _stream(w.device))
+    return codes, steps, amb
+
+
+def repack_fp8(codes: torch.Tensor, steps: torch.Tensor, fmt="e4m3"):
+    """q4 grid -> (FP8 codes u8 [N,K], per-channel scale f32 [N])."""
+    _check(codes, "codes", torch.uint8, 2)
+    _check(steps, "steps", torch.bfloat16, 2)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    wq = torch.empty((N, K), dtype=torch.uint8, device=codes.device)
+    ws = torch.empty(N, dtype=torch.float32, device=codes.device)
+    _call("qlin_repack_fp8", _ptr(codes), _ptr(steps), N, K, _FMT[fmt], _ptr(wq), _ptr(ws),
+          _stream(codes.device))
+    return wq, ws
+
+
+def repack_int8(codes: torch.Tensor, steps: torch.Tensor):
+    _check(codes, "codes", torch.uint8, 2)
+    _check(steps, "steps", torch.bfloat16, 2)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    wq = torch.empty((N, K), dtype=torch.int8, device=codes.device)
+    ws = torch.empty(N, dtype=torch.float32, device=codes.device)
+    _call("qlin_repack_int8", _ptr(codes), _ptr(steps), N, K, _ptr(wq), _ptr(ws),
+          _stream(codes.device))
+    return wq, ws
+
+
+def fp8_fnuz_to_ocp(w_fnuz: torch.Tensor, s_in: torch.Tensor):
+    """E4M3FNUZ weights + scales -> (OCP codes, scales, n_inexact int64 [1])."""
+    _check(w_fnuz, "w_fnuz", torch.uint8, 2)
+    _check(s_in, "s_in", torch.float32, 1)
+    N, K = w_fnuz.shape
+    wo = torch.empty_like(w_fnuz)
+    so = torch.empty_like(s_in)
+    bad = torch.empty(1, dtype=torch.int64, device=w_fnuz.device)
+    _call("qlin_fp8_fnuz_to_ocp", _ptr(w_fnuz), _ptr(s_in), N, K, _ptr(wo), _ptr(so), _ptr(bad),
+          _stream(w_fnuz.device))
+    return wo, so, bad
+
+
+def dequant_q4_bf16(codes: torch.Tensor, steps: torch.Tensor) -> torch.Tensor:
+    _check(codes, "codes", torch.uint8, 2)
+    _check(steps, "steps", torch.bfloat16, 2)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=codes.device)
+    _call("qlin_dequant_q4_bf16", _ptr(codes), _ptr(steps), N, K, _ptr(out), _stream(codes.device))
+    return out
+
+
+# ---------------------------------------------------------------- quantisers
+def quant_act(a: torch.Tensor, fmt="e4m3", out=None):
+    """bf16 [M,K] (row stride may exceed K) -> (codes [M,K], scale f32 [M]).
+    `out` may pass preallocated (codes, scale) tensors."""
+    if not (isinstance(a, torch.Tensor) and a.is_cuda and a.dtype == torch.bfloat16 and a.dim() == 2
+            and a.stride(1) == 1):
+        raise ValueError("a must be a 2-D bf16 device tensor with unit column stride")
+    M, K = a.shape
+    f = _FMT[fmt]
+    if out is not None:
+        q, s = out
+        _check(q, "out codes", torch.int8 if f == INT8 else torch.uint8, 2)
+        _check(s, "out scale", torch.float32, 1)
+        if q.shape != (M, K) or s.numel() != M:
+            raise ValueError("out shape mismatch")
+    else:
+        q = torch.empty((M, K), dtype=torch.int8 if f == INT8 else torch.uint8, device=a.device)
+        s = torch.empty(M, dtype=torch.float32, device=a.device)
+    _call("qlin_quant_act", _ptr(a), M, K, a.stride(0), f, _ptr(q), _ptr(s), _stream(a.device))
+    return q, s
+
+
+def fp8_encode_f32(x: torch.Tensor, fmt="e4m3") -> torch.Tensor:
+    _check(x, "x", torch.float32)
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _call("qlin_fp8_encode_f32", _ptr(x), x.numel(), _FMT[fmt], _ptr(out), _stream(x.device))
+    return out
+
+
+# ---------------------------------------------------------------- GEMMs
+def _out(M, N, dev, out_dtype):
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    return torch.empty((M, N), dtype=out_dtype, device=dev), (OUT_F32 if out_dtype == torch.float32
+                                                              else OUT_BF16)
+
+
+def gemm_fp8(a_q, a_scale, w_q, w_scale, out_dtype=torch.bfloat16, out=None):
+    """Y = ((A_q . W_q^T) * a_scale[:,None]) * w_scale[None,:], OCP E4M3."""
+    _check(a_q, "a_q", torch.uint8, 2)
+    _check(w_q, "w_q", torch.uint8, 2)
+    _check(a_scale, "a_scale", torch.float32, 1)
+    _check(w_scale, "w_scale", torch.float32, 1)
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K or a_scale.numel() != M or w_scale.numel() != N:
+        raise ValueError("shape mismatch")
+    y, od = (out, OUT_F32 if out.dtype == torch.float32 else OUT_BF16) if out is not None else \
+        _out(M, N, a_q.device, out_dtype)
+    nb = workspace_bytes(OP_GEMM_FP8, M, N, K)
+    ws = workspace(nb, a_q.device)
+    _call("qlin_gemm_fp8", _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), M, N, K, _ptr(y), od,
+          _ptr(ws), ws.numel(), _stream(a_q.device))
+    return y
+
+
+def gemm_w8a8(a_q, a_scale, w_q, w_scale, out_dtype=torch.bfloat16, out=None):
+    """Y = ((float)(A_q . W_q^T) * a_scale) * w_scale, int32 accumulation."""
+    _check(a_q, "a_q", torch.int8, 2)
+    _check(w_q, "w_q", torch.int8, 2)
+    _check(a_scale, "a_scale", torch.float32, 1)
+    _check(w_scale, "w_scale", torch.float32, 1)
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K or a_scale.numel() != M or w_scale.numel() != N:
+        raise ValueError("shape mismatch")
+    y, od = (out, OUT_F32 if out.dtype == torch.float32 else OUT_BF16) if out is not None else \
+        _out(M, N, a_q.device, out_dtype)
+    nb = workspace_bytes(OP_GEMM_W8A8, M, N, K)
+    ws = workspace(nb, a_q.device)
+    _call("qlin_gemm_w8a8", _ptr(a_q), _ptr(a_scale), _ptr(w_q), _ptr(w_scale), M, N, K, _ptr(y),
+          od, _ptr(ws), ws.numel(), _stream(a_q.device))
+    return y
+
+
+def gemm_w4a16(a, codes, steps, out_dtype=torch.bfloat16, out=None):
+    """Y = A . bf16(c * step)^T with group-32 int4 weights, bf16 activations."""
+    if not (isinstance(a, torch.Tensor) and a.is_cuda and a.dtype == torch.bfloat16 and a.dim() == 2
+            and a.stride(1) == 1):
+        raise ValueError("a must be a 2-D bf16 device tensor with unit column stride")
+    _check(codes, "codes", torch.uint8, 2)
+    _check(steps, "steps", torch.bfloat16, 2)
+    M, K = a.shape
+    N = codes.shape[0]
+    if codes.shape[1] * 2 != K or steps.shape != (N, K // 32):
+        raise ValueError("shape mismatch")
+    y, od = (out, OUT_F32 if out.dtype == torch.float32 else OUT_BF16) if out is not None else \
+        _out(M, N, a.device, out_dtype)
+    nb = workspace_bytes(OP_GEMM_W4A16, M, N, K)
+    ws = workspace(nb, a.device)
+    _call("qlin_gemm_w4a16", _ptr(a), a.stride(0), _ptr(codes), _ptr(steps), M, N, K, _ptr(y), od,
+          _ptr(ws), ws.numel(), _stream(a.device))
+    return y
+
+
+def _linear(name, op, x, w_q, w_scale, wdtype):
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2
+            and x.stride(1) == 1):
+        raise ValueError("x must be a 2-D bf16 device tensor with unit column stride")
+    _check(w_q, "w_q", wdtype, 2)
+    _check(w_scale, "w_scale", torch.float32, 1)
+    M, K = x.shape
+    N = w_q.shape[0]
+    if w_q.shape[1] != K or w_scale.numel() != N:
+        raise ValueError("shape mismatch")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    ws = workspace(workspace_bytes(op, M, N, K), x.device)
+    _call(name, _ptr(x), x.stride(0), _ptr(w_q), _ptr(w_scale), M, N, K, _ptr(y), _ptr(ws),
+          ws.numel(), _stream(x.device))
+    return y
+
+
+def linear_fp8(x, w_q, w_scale):
+    """Per-token FP8 quantisation of x followed by the FP8 GEMM (bf16 out)."""
+    return _linear("qlin_linear_fp8", OP_LINEAR_FP8, x, w_q, w_scale, torch.uint8)
+
+
+def linear_w8a8(x, w_q, w_scale):
+    """Per-token int8 quantisation of x followed by the int8 GEMM."""
+    return _linear("qlin_linear_w8a8", OP_LINEAR_W8A8, x, w_q, w_scale, torch.int8)
+
+
+# ---------------------------------------------------------------- MoE
+def moe_workspace_layout(T, H, I, E, topk):
+    offs = (C.c_size_t * 6)()
+    _call("qlin_moe_workspace_layout", T, H, I, E, topk, offs)
+    return [int(o) for o in offs]
+
+
+def moe_fp8(x, topk_ids, topk_w, w13, s13, w2, s2, return_stages=False):
+    """FP8 MoE block. x [T,H] bf16; topk_ids int32 [T,k]; topk_w f32 [T,k];
+    w13 u8 [E,2I,H], s13 f32 [E,2I]; w2 u8 [E,H,I], s2 f32 [E,H]."""
+    _check(x, "x", torch.bfloat16, 2)
+    _check(topk_ids, "topk_ids", torch.int32, 2)
+    _check(topk_w, "topk_w", torch.float32, 2)
+    _check(w13, "w13", torch.uint8, 3)
+    _check(s13, "s13", torch.float32, 2)
+    _check(w2, "w2", torch.uint8, 3)
+    _check(s2, "s2", torch.float32, 2)
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    topk = topk_ids.shape[1]
+    if H2 != H or w2.shape != (E, H, I) or s13.shape != (E, I2) or s2.shape != (E, H) or \
+            topk_w.shape != topk_ids.shape or topk_ids.shape[0] != T:
+        raise ValueError("shape mismatch")
+    nb = int(_lib.qlin_moe_workspace_bytes(T, H, I, E, topk))
+    ws = workspace(nb, x.device) if not return_stages else \
+        torch.empty(max(nb, 256), dtype=torch.uint8, device=x.device)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _call("qlin_moe_fp8", _ptr(x), T, H, I, E, topk, _ptr(topk_ids), _ptr(topk_w), _ptr(w13),
+          _ptr(s13), _ptr(w2), _ptr(s2), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device))
+    if not return_stages:
+        return y
+    o = moe_workspace_layout(T, H, I, E, topk)
+    R = T * topk
+
+    def view(off, n, dt):
+        return ws[off: off + n * torch.tensor([], dtype=dt).element_size()].view(dt)
+
+    stages = dict(xq=view(o[0], T * H, torch.uint8).view(T, H), sx=view(o[1], T, torch.float32),
+                  act=view(o[2], R * I, torch.float32).view(R, I),
+                  aq=view(o[3], R * I, torch.uint8).view(R, I), sa=view(o[4], R, torch.float32),
+                  d=view(o[5], R * H, torch.float32).view(R, H))
+    return y, stages

@@ -1,0 +1,267 @@
+// FP8 mixture-of-experts block for gfx950 ("Gemma 4 From E2B to 31B",
+// "Step 1 -- Build the Larger Repacks": the fused expert banks gate_up_proj /
+// down_proj are split per expert and quantised like the dense layers, the
+// router stays outside in bf16; vLLM PR #45854 report: the fp8 MoE takes
+// per-token activation and per-output-channel weight scales).
+//
+// Stages (one kernel each; intermediates live in the workspace):
+//   1. per-token FP8 quant of x                    -> xq [T][H], sx [T]
+//   2. routing bookkeeping (one workgroup): rows of each expert
+//   3. grouped gate_up: for every touched expert, its 2I x H FP8 weights are
+//      streamed once for all of its rows; h = (xq.w13^T)*sx*s13, then
+//      act = SiLU(h[:I]) * h[I:] in fp32        -> act [R][I]   (R = T*topk)
+//   4. per-row FP8 requant of act                 -> aq [R][I], sa [R]
+//   5. grouped down: d = (aq.w2^T)*sa*s2           -> d [R][H] fp32
+//   6. combine: y[t] = bf16(sum_j p[t,j] * d[t*topk+j]) in slot order.
+// Experts that no token routes to are never read.
+#include "qlin_device.h"
+#include "qlin_internal.h"
+
+namespace qlin {
+
+MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk) {
+  const int64_t R = T * topk;
+  MoeLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes, 256);
+    return at;
+  };
+  L.xq = take((size_t)T * H);
+  L.sx = take((size_t)T * 4);
+  L.act = take((size_t)R * I * 4);
+  L.aq = take((size_t)R * I);
+  L.sa = take((size_t)R * 4);
+  L.d = take((size_t)R * H * 4);
+  L.cnt = take((size_t)E * 4);
+  L.off = take((size_t)(E + 1) * 4);
+  L.rows = take((size_t)R * 4);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------- routing
+// off[e] = first position of expert e in rows[]; rows[] lists r = t*topk+j.
+// The order of rows inside an expert does not affect any result (every
+// output row is computed from its own activation row only).
+__global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restrict__ ids, int R,
+                                                         int E, int* __restrict__ off,
+                                                         int* __restrict__ rows) {
+  extern __shared__ int sh[];  // cnt[E], cur[E]
+  int* cnt = sh;
+  int* cur = sh + E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const int e = ids[r];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e] = run;
+      cur[e] = run;
+      run += cnt[e];
+    }
+    off[E] = run;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const int e = ids[r];
+    if (e >= 0 && e < E) rows[atomicAdd(&cur[e], 1)] = r;
+  }
+}
+
+// ---------------------------------------------------------------- grouped GEMM
+struct MoeGemmArgs {
+  const uint8_t* A;    // gate_up: xq [T][H]; down: aq [R][I]
+  const float* sa;     // gate_up: sx [T]; down: sa [R]
+  const uint8_t* W;    // gate_up: w13 [E][2I][H]; down: w2 [E][H][I]
+  const float* sw;     // s13 [E][2I] / s2 [E][H]
+  const int* off;      // [E+1]
+  const int* rows;     // [R]
+  int topk;
+  int K;               // H (gate_up) or I (down)
+  int nout;            // I (gate_up: pairs) or H (down)
+  float* out;          // act [R][I] or d [R][H]
+};
+
+constexpr int kMoeNW = 4;
+constexpr int kMoeDepth = 4;
+constexpr int kMoeKA = 512;
+
+// One wave owns 16 output columns of one expert (gate_up: 16 gate rows and
+// the matching 16 up rows), the workgroup 64 columns, for up to MB*16 rows.
+template <bool GATEUP, int MB>
+__device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, int nrows,
+                                         uint8_t* lds) {
+  constexpr int NB = GATEUP ? 2 : 1;
+  constexpr int kRowBytes = kMoeKA + 16;
+  constexpr int kStepsPerChunk = kMoeKA / 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = p.K;
+  const int col = blockIdx.x * (kMoeNW * 16) + wave * 16 + r;  // output column of this lane
+  const int colc = min(col, p.nout - 1);
+  const size_t wrows = GATEUP ? 2 * (size_t)p.nout : (size_t)p.nout;
+  const uint8_t* wbase = p.W + (size_t)e * wrows * K;
+  const uint8_t* wr[NB];
+  wr[0] = wbase + (size_t)colc * K;
+  if (GATEUP) wr[NB - 1] = wbase + (size_t)(p.nout + colc) * K;
+
+  v4f acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+
+  const int nsteps = (K + 127) / 128;
+  uint4 wlo[kMoeDepth][NB], whi[kMoeDepth][NB];
+  auto loadw = [&](int slot, int s) {
+    const int ka = s * 128 + 16 * g, kb = ka + 64;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      wlo[slot][j] = ka < K ? ldg16_nt(wr[j] + ka) : make_uint4(0, 0, 0, 0);
+      whi[slot][j] = kb < K ? ldg16_nt(wr[j] + kb) : make_uint4(0, 0, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < kMoeDepth; ++d)
+    if (d < nsteps) loadw(d, d);
+
+  for (int c0 = 0; c0 < nsteps; c0 += kStepsPerChunk) {
+    __syncthreads();
+    {
+      constexpr int kPieces = MB * 16 * (kMoeKA / 16);
+      for (int i = tid; i < kPieces; i += kMoeNW * 64) {
+        const int row = i / (kMoeKA / 16), pc = i % (kMoeKA / 16);
+        const int k = c0 * 128 + pc * 16;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < nrows && k < K) {
+          const int rr = p.rows[rbeg + row];
+          const int arow = GATEUP ? rr / p.topk : rr;
+          v = ldg16(p.A + (size_t)arow * K + k);
+        }
+        *reinterpret_cast<uint4*>(lds + row * kRowBytes + pc * 16) = v;
+      }
+    }
+    __syncthreads();
+    const int cend = min(c0 + kStepsPerChunk, nsteps);
+    for (int s0 = c0; s0 < cend; s0 += kMoeDepth) {
+#pragma unroll
+      for (int d = 0; d < kMoeDepth; ++d) {
+        const int s = s0 + d;
+        if (s < cend) {
+          const int sl = s - c0;
+#pragma unroll
+          for (int i = 0; i < MB; ++i) {
+            const uint8_t* ap = lds + (i * 16 + r) * kRowBytes + sl * 128 + 16 * g;
+            const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
+            const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 64);
+            const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+              const v8i wv = {(int)wlo[d][j].x, (int)wlo[d][j].y, (int)wlo[d][j].z, (int)wlo[d][j].w,
+                              (int)whi[d][j].x, (int)whi[d][j].y, (int)whi[d][j].z, (int)whi[d][j].w};
+              acc[i][j] = mfma_fp8(av, wv, acc[i][j]);
+            }
+          }
+          if (s + kMoeDepth < nsteps) loadw(d, s + kMoeDepth);
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds rows 4g+e (per block), column `col`
+  if (col < p.nout) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = i * 16 + 4 * g + q;
+        if (row < nrows) {
+          const int rr = p.rows[rbeg + row];
+          if (GATEUP) {
+            const int t = rr / p.topk;
+            float gv = (acc[i][0][q] * p.sa[t]) * p.sw[(size_t)e * 2 * p.nout + col];
+            float uv = (acc[i][1][q] * p.sa[t]) * p.sw[(size_t)e * 2 * p.nout + p.nout + col];
+            const float silu = gv / (1.0f + expf(-gv));
+            p.out[(size_t)rr * p.nout + col] = silu * uv;
+          } else {
+            p.out[(size_t)rr * p.nout + col] =
+                (acc[i][0][q] * p.sa[rr]) * p.sw[(size_t)e * p.nout + col];
+          }
+        }
+      }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kMoeNW * 64) void moe_gemm_kernel(const MoeGemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[64 * (kMoeKA + 16)];
+  const int e = blockIdx.y;
+  const int beg = p.off[e], n = p.off[e + 1] - beg;
+  for (int rb = 0; rb < n; rb += 64) {
+    const int nr = min(64, n - rb);
+    const int mb = (nr + 15) / 16;
+    if (mb == 1) moe_tile<GATEUP, 1>(p, e, beg + rb, nr, lds);
+    else if (mb == 2) moe_tile<GATEUP, 2>(p, e, beg + rb, nr, lds);
+    else if (mb == 3) moe_tile<GATEUP, 3>(p, e, beg + rb, nr, lds);
+    else moe_tile<GATEUP, 4>(p, e, beg + rb, nr, lds);
+  }
+}
+
+// ---------------------------------------------------------------- combine
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ d,
+                                                          const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ wts, int topk,
+                                                          int H, int E, uint16_t* __restrict__ y) {
+  const int t = blockIdx.x;
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float acc = 0.0f;
+    for (int j = 0; j < topk; ++j) {
+      const int e = ids[t * topk + j];
+      if (e >= 0 && e < E) acc = acc + wts[t * topk + j] * d[((size_t)t * topk + j) * H + h];
+    }
+    y[(size_t)t * H + h] = (uint16_t)f32_bf16_rne(acc);
+  }
+}
+
+int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                   const int32_t* ids, const float* wts, const uint8_t* w13, const float* s13,
+                   const uint8_t* w2, const float* s2, uint16_t* y, void* ws, hipStream_t st) {
+  const MoeLayout L = moe_layout(T, H, I, E, topk);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  uint8_t* xq = base + L.xq;
+  float* sx = reinterpret_cast<float*>(base + L.sx);
+  float* act = reinterpret_cast<float*>(base + L.act);
+  uint8_t* aq = base + L.aq;
+  float* sa = reinterpret_cast<float*>(base + L.sa);
+  float* dd = reinterpret_cast<float*>(base + L.d);
+  int* off = reinterpret_cast<int*>(base + L.off);
+  int* rows = reinterpret_cast<int*>(base + L.rows);
+  const int R = (int)(T * topk);
+
+  int rc = launch_quant_act(x, T, H, H, QLIN_E4M3, xq, sx, st);
+  if (rc) return rc;
+  moe_route_kernel<<<1, 1024, 2 * E * sizeof(int), st>>>(ids, R, (int)E, off, rows);
+  if ((rc = launch_status())) return rc;
+
+  MoeGemmArgs gu{xq, sx, w13, s13, off, rows, topk, (int)H, (int)I, act};
+  moe_gemm_kernel<true><<<dim3((unsigned)((I + 63) / 64), (unsigned)E), kMoeNW * 64, 0, st>>>(gu);
+  if ((rc = launch_status())) return rc;
+
+  if ((rc = launch_quant_rows_f32(act, R, I, aq, sa, st))) return rc;
+
+  MoeGemmArgs dn{aq, sa, w2, s2, off, rows, topk, (int)I, (int)H, dd};
+  moe_gemm_kernel<false><<<dim3((unsigned)((H + 63) / 64), (unsigned)E), kMoeNW * 64, 0, st>>>(dn);
+  if ((rc = launch_status())) return rc;
+
+  moe_combine_kernel<<<dim3((unsigned)T), 256, 0, st>>>(dd, ids, wts, topk, (int)H, (int)E, y);
+  return launch_status();
+}
+
+}  // namespace qlin

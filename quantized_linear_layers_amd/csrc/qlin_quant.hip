@@ -1,0 +1,203 @@
+// Dynamic per-token activation quantisation for gfx950 (Gemma 4 31B-it FP8
+// model card: activations quantised to FP8 per token at run time; "Gemma 4
+// From E2B to 31B" article, format table: int8 activations per token).
+//   s = max_k |a| / FMAX   (FMAX 448 for OCP E4M3, 127 for int8)
+//   q = nearest-even E4M3 code of a / s (saturating)  or  clamp(rint(a/s)).
+// One workgroup per row; the row is read once into registers (up to 16384
+// elements), reduced to its absmax, then encoded and written.
+#include "qlin_device.h"
+#include "qlin_internal.h"
+
+namespace qlin {
+
+constexpr int kQThreads = 256;
+
+// 8 fp32 values -> 8 code bytes (two 32-bit words).
+template <int FMT>
+__device__ __forceinline__ uint2 encode8(const float (&v)[8]) {
+  uint32_t w[2];
+  if (FMT == QLIN_E4M3) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      w[h] = fp8_encode_hw2(v[4 * h], v[4 * h + 1]) | (fp8_encode_hw2(v[4 * h + 2], v[4 * h + 3]) << 16);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      w[h] = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t b = FMT == QLIN_INT8 ? ((uint32_t)int8_code(v[4 * h + i]) & 0xFFu)
+                                      : fp8_encode<true>(v[4 * h + i]);
+        w[h] |= b << (8 * i);
+      }
+    }
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& x, float (&v)[8]) {
+  const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(xs[i] << 16);
+    v[2 * i + 1] = __uint_as_float(xs[i] & 0xFFFF0000u);
+  }
+}
+
+// CMAX > 0: the row (K/8 chunks of 8 bf16) is held in registers, CMAX chunks
+// per lane. CMAX == 0: two passes over global memory (rows longer than
+// 16384 elements).
+template <int FMT, int CMAX>
+__global__ __launch_bounds__(kQThreads) void quant_act_kernel(const uint16_t* __restrict__ a,
+                                                              int64_t K, int64_t lda,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  __shared__ float red[kQThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint16_t* row = a + m * lda;
+  uint8_t* qrow = q + m * K;
+  const int chunks = (int)(K / 8);
+  constexpr float kFmax = FMT == QLIN_INT8 ? 127.0f : (FMT == QLIN_E4M3FNUZ ? 240.0f : 448.0f);
+  float amax = 0.0f;
+  if (CMAX > 0) {
+    uint4 cache[CMAX > 0 ? CMAX : 1];
+#pragma unroll
+    for (int c = 0; c < CMAX; ++c) {
+      const int idx = threadIdx.x + c * kQThreads;
+      cache[c] = idx < chunks ? ldg16(row + (int64_t)idx * 8) : make_uint4(0, 0, 0, 0);
+      float v[8];
+      unpack_bf16x8(cache[c], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = block_max<kQThreads / 64>(amax, red);
+    const float sc = amax > 0.0f ? amax / kFmax : 0.0f;
+#pragma unroll
+    for (int c = 0; c < CMAX; ++c) {
+      const int idx = threadIdx.x + c * kQThreads;
+      if (idx < chunks) {
+        uint2 out = make_uint2(0, 0);
+        if (sc > 0.0f) {
+          float v[8];
+          unpack_bf16x8(cache[c], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = v[i] / sc;
+          out = encode8<FMT>(v);
+        }
+        *reinterpret_cast<uint2*>(qrow + (int64_t)idx * 8) = out;
+      }
+    }
+    if (threadIdx.x == 0) s[m] = sc;
+  } else {
+    for (int idx = threadIdx.x; idx < chunks; idx += kQThreads) {
+      float v[8];
+      unpack_bf16x8(ldg16(row + (int64_t)idx * 8), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+    amax = block_max<kQThreads / 64>(amax, red);
+    const float sc = amax > 0.0f ? amax / kFmax : 0.0f;
+    for (int idx = threadIdx.x; idx < chunks; idx += kQThreads) {
+      uint2 out = make_uint2(0, 0);
+      if (sc > 0.0f) {
+        float v[8];
+        unpack_bf16x8(ldg16(row + (int64_t)idx * 8), v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] / sc;
+        out = encode8<FMT>(v);
+      }
+      *reinterpret_cast<uint2*>(qrow + (int64_t)idx * 8) = out;
+    }
+    if (threadIdx.x == 0) s[m] = sc;
+  }
+}
+
+template <int FMT>
+static void launch_quant_fmt(const uint16_t* a, int64_t M, int64_t K, int64_t lda, uint8_t* q,
+                             float* s, hipStream_t st) {
+  const int64_t chunks = K / 8;
+  const dim3 grid((unsigned)M);
+  if (chunks <= 1 * kQThreads)
+    quant_act_kernel<FMT, 1><<<grid, kQThreads, 0, st>>>(a, K, lda, q, s);
+  else if (chunks <= 2 * kQThreads)
+    quant_act_kernel<FMT, 2><<<grid, kQThreads, 0, st>>>(a, K, lda, q, s);
+  else if (chunks <= 4 * kQThreads)
+    quant_act_kernel<FMT, 4><<<grid, kQThreads, 0, st>>>(a, K, lda, q, s);
+  else if (chunks <= 8 * kQThreads)
+    quant_act_kernel<FMT, 8><<<grid, kQThreads, 0, st>>>(a, K, lda, q, s);
+  else
+    quant_act_kernel<FMT, 0><<<grid, kQThreads, 0, st>>>(a, K, lda, q, s);
+}
+
+int launch_quant_act(const uint16_t* a, int64_t M, int64_t K, int64_t lda, int fmt, void* q,
+                     float* s, hipStream_t st) {
+  uint8_t* qb = reinterpret_cast<uint8_t*>(q);
+  if (fmt == QLIN_INT8) launch_quant_fmt<QLIN_INT8>(a, M, K, lda, qb, s, st);
+  else if (fmt == QLIN_E4M3FNUZ) launch_quant_fmt<QLIN_E4M3FNUZ>(a, M, K, lda, qb, s, st);
+  else launch_quant_fmt<QLIN_E4M3>(a, M, K, lda, qb, s, st);
+  return launch_status();
+}
+
+// fp32 rows -> OCP E4M3 (the MoE intermediate): same rule, rows of K fp32.
+__global__ __launch_bounds__(kQThreads) void quant_rows_f32_kernel(const float* __restrict__ a,
+                                                                   int64_t K,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ s) {
+  __shared__ float red[kQThreads / 64];
+  const int64_t m = blockIdx.x;
+  const float* row = a + m * K;
+  const int chunks = (int)(K / 8);
+  float amax = 0.0f;
+  for (int idx = threadIdx.x; idx < chunks; idx += kQThreads) {
+    const float4 x0 = *reinterpret_cast<const float4*>(row + (int64_t)idx * 8);
+    const float4 x1 = *reinterpret_cast<const float4*>(row + (int64_t)idx * 8 + 4);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x0.x), fabsf(x0.y)), fmaxf(fabsf(x0.z), fabsf(x0.w))));
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x1.x), fabsf(x1.y)), fmaxf(fabsf(x1.z), fabsf(x1.w))));
+  }
+  amax = block_max<kQThreads / 64>(amax, red);
+  const float sc = amax > 0.0f ? amax / 448.0f : 0.0f;
+  for (int idx = threadIdx.x; idx < chunks; idx += kQThreads) {
+    uint2 out = make_uint2(0, 0);
+    if (sc > 0.0f) {
+      const float4 x0 = *reinterpret_cast<const float4*>(row + (int64_t)idx * 8);
+      const float4 x1 = *reinterpret_cast<const float4*>(row + (int64_t)idx * 8 + 4);
+      float v[8] = {x0.x / sc, x0.y / sc, x0.z / sc, x0.w / sc,
+                    x1.x / sc, x1.y / sc, x1.z / sc, x1.w / sc};
+      out = encode8<QLIN_E4M3>(v);
+    }
+    *reinterpret_cast<uint2*>(q + m * K + (int64_t)idx * 8) = out;
+  }
+  if (threadIdx.x == 0) s[m] = sc;
+}
+
+int launch_quant_rows_f32(const float* a, int64_t M, int64_t K, uint8_t* q, float* s,
+                          hipStream_t st) {
+  quant_rows_f32_kernel<<<dim3((unsigned)M), kQThreads, 0, st>>>(a, K, q, s);
+  return launch_status();
+}
+
+// Element-wise encoder (the quantisers' codec), 8 values per lane.
+template <int FMT>
+__global__ __launch_bounds__(256) void fp8_encode_kernel(const float* __restrict__ x, int64_t n,
+                                                         uint8_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i >= n) return;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (i + j < n) ? x[i + j] : 0.0f;
+  const uint2 w = encode8<FMT>(v);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (i + j < n) out[i + j] = (uint8_t)(((j < 4 ? w.x : w.y) >> (8 * (j & 3))) & 0xFFu);
+}
+
+int launch_fp8_encode(const float* x, int64_t n, int fmt, uint8_t* out, hipStream_t st) {
+  const int64_t blocks = (n + 8 * 256 - 1) / (8 * 256);
+  if (fmt == QLIN_E4M3FNUZ)
+    fp8_encode_kernel<QLIN_E4M3FNUZ><<<dim3((unsigned)blocks), 256, 0, st>>>(x, n, out);
+  else
+    fp8_encode_kernel<QLIN_E4M3><<<dim3((unsigned)blocks), 256, 0, st>>>(x, n, out);
+  return launch_status();
+}
+
+}  // namespace qlin
