@@ -160,12 +160,14 @@ int qlin_quant_act(const qlin_bf16* a, int64_t M, int64_t K, int64_t lda, int fm
 int qlin_fp8_encode_f32(const float* x, int64_t n, int fmt, uint8_t* out, qlin_stream_t stream);
 
 /* ------------------------------------------------------------------------
- * GEMMs. Workspace: the split-K paths keep fp32/int32 partial sums and
- * per-tile arrival counters in a caller-provided workspace of
- * qlin_workspace_bytes(op, M, N, K) bytes (256-byte aligned). The counter
- * area must be ZERO before the first call that uses the workspace (allocate
- * it zeroed, or call qlin_workspace_init); every call leaves it zero again.
- * Calls that share one workspace must be ordered on one stream.
+ * GEMMs. Workspace: the split-K paths keep per-tile arrival counters (the
+ * first 64 KiB) and fp32/int32 partial sums (after them) in a caller-provided
+ * workspace of qlin_workspace_bytes(op, M, N, K) bytes (256-byte aligned;
+ * 0 means none is needed). The counter area must be ZERO before the first
+ * call that uses the workspace (allocate it zeroed, or call
+ * qlin_workspace_init); every call leaves it zero again, whatever its shape,
+ * so one zeroed workspace serves all later calls. Calls that share one
+ * workspace must be ordered on one stream.
  * ------------------------------------------------------------------------ */
 size_t qlin_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 

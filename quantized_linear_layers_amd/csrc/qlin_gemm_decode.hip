@@ -23,6 +23,8 @@
 //    the workspace and the last workgroup of a column tile to arrive (device-
 //    scope counter) sums them in split order, so results are deterministic,
 //    applies the epilogue and resets the counter.
+#include <stdlib.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -127,6 +129,17 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
     ap[mb] = p.A + (size_t)min(row, p.M - 1) * p.lda * (KIND == kGemmW4 ? 2 : 1);
     amask[mb] = row < p.M ? 0xFFFFFFFFu : 0u;
   }
+
+  // epilogue scales of this lane's rows / columns, fetched up front (clamped
+  // addresses, no branches) so that their latency hides under the main loop
+  float sav[MB][4], swv[NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sav[mb][i] = KIND == kGemmW4 ? 1.0f : p.sa[min(mb * 16 + 4 * g + i, p.M - 1)];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) swv[j] = KIND == kGemmW4 ? 1.0f : p.sw[min(n0 + 16 * j + r, p.N - 1)];
 
   auto load = [&](Slot<KIND, MB, NB>& sl, int t) {
     const int kb = kw0 + t * 128;
@@ -291,27 +304,41 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
     old = __shfl(old, 0, kWave);
     if (old != (unsigned)(S - 1)) return;
     __threadfence();
+    // sum the splits in split order; every load of one split is issued
+    // before the first is consumed (clamped addresses, no branches)
+    const size_t stride = (size_t)p.M * p.N;
+    uint32_t off[MB][NB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          off[mb][j][i] = (uint32_t)((size_t)min(mb * 16 + 4 * g + i, p.M - 1) * p.N +
+                                     min(n0 + 16 * j + r, p.N - 1));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = mb * 16 + 4 * g + i, n = n0 + 16 * j + r;
-          if (m < p.M && n < p.N) {
-            const uint32_t* q = p.part + (size_t)m * p.N + n;
-            const size_t stride = (size_t)p.M * p.N;
-            if constexpr (KIND == kGemmI8) {
-              int v = (int)q[0];
-              for (int s = 1; s < S; ++s) v += (int)q[s * stride];
-              acci[mb][j][i] = v;
-            } else {
-              float v = __uint_as_float(q[0]);
-              for (int s = 1; s < S; ++s) v = v + __uint_as_float(q[s * stride]);
-              accf[mb][j][i] = v;
-            }
-          }
+          const uint32_t u = p.part[off[mb][j][i]];
+          if constexpr (KIND == kGemmI8) acci[mb][j][i] = (int)u;
+          else accf[mb][j][i] = __uint_as_float(u);
         }
+    for (int s = 1; s < S; ++s) {
+      const uint32_t* q = p.part + (size_t)s * stride;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t u = q[off[mb][j][i]];
+            if constexpr (KIND == kGemmI8) acci[mb][j][i] += (int)u;
+            else accf[mb][j][i] = accf[mb][j][i] + __uint_as_float(u);
+          }
+    }
     if (lane == 0) p.cnt[blockIdx.x] = 0u;
   }
 
@@ -326,8 +353,8 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
         if (m < p.M && n < p.N) {
           float v;
           if constexpr (KIND == kGemmW4) v = accf[mb][j][i];
-          else if constexpr (KIND == kGemmI8) v = ((float)acci[mb][j][i] * p.sa[m]) * p.sw[n];
-          else v = (accf[mb][j][i] * p.sa[m]) * p.sw[n];
+          else if constexpr (KIND == kGemmI8) v = ((float)acci[mb][j][i] * sav[mb][i]) * swv[j];
+          else v = (accf[mb][j][i] * sav[mb][i]) * swv[j];
           if (p.out_f32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = v;
           else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = (uint16_t)f32_bf16_rne(v);
         }
@@ -363,16 +390,25 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   int64_t S = (2048 + waves - 1) / waves;
   S = std::min<int64_t>(S, std::max<int64_t>(1, ksteps / ((int64_t)c.NWK * c.DEPTH)));
   S = std::max<int64_t>(1, std::min<int64_t>(S, 8));
+  if (const char* e = getenv("QLIN_DECODE_SPLIT")) S = std::max(1, atoi(e));  // tuning override
+  if (c.tiles > 16384) S = 1;  // counter area bound; such grids need no split
   const int64_t steps_per = (ksteps + S - 1) / S;
   c.kc = (int)(steps_per * 128);
   c.S = (int)((K + c.kc - 1) / c.kc);
   return c;
 }
 
+// Workspace of a split-K call: a fixed counter area (one word per column
+// tile, at most kMaxTiles) at offset 0, then the partial sums. Every call
+// leaves the counter area zero, and no call ever writes partials there, so a
+// workspace zeroed once stays valid across calls of any shape.
+constexpr int kMaxTiles = 16384;
+constexpr size_t kCounterBytes = (size_t)kMaxTiles * 4;
+
 size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K) {
   const DecodeCfg c = decode_cfg(kind, M, N, K);
   if (c.S <= 1) return 0;
-  return round_up((size_t)c.S * M * N * 4, 256) + round_up((size_t)c.tiles * 4, 256);
+  return kCounterBytes + round_up((size_t)c.S * M * N * 4, 256);
 }
 
 template <int KIND, int MB, int NB, int DEPTH>
@@ -419,9 +455,8 @@ int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const v
   g.out_f32 = out_f32;
   if (c.S > 1) {
     if (!ws || ws_bytes < decode_workspace_bytes(kind, M, N, K)) return QLIN_ERR_WORKSPACE;
-    g.part = reinterpret_cast<uint32_t*>(ws);
-    g.cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(ws) +
-                                        round_up((size_t)c.S * M * N * 4, 256));
+    g.cnt = reinterpret_cast<unsigned*>(ws);
+    g.part = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kCounterBytes);
   }
   if (kind == kGemmFP8) launch_decode_kind<kGemmFP8>(g, c, st);
   else if (kind == kGemmI8) launch_decode_kind<kGemmI8>(g, c, st);

