@@ -14,7 +14,7 @@
 //  * a workgroup of NWK waves owns 16*NB output columns and one K range;
 //    its waves take consecutive slices of the range (split-K across
 //    workgroups as well when the grid would otherwise be too small);
-//  * each wave streams its 16*NB weight rows (16-byte nontemporal loads) and
+//  * each wave streams its 16*NB weight rows (16-byte loads) and
 //    its activation rows (L2-resident) into registers, DEPTH 128-wide K steps
 //    ahead of use, with branch-free loads;
 //  * MFMA with M padded to 16 (padding rows masked to zero);
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
       const int kg = min(kb + 32 * g, kclamp);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        sl.w[j] = ldg16_nt(wp[j] + (kg >> 1));
+        sl.w[j] = ldg16(wp[j] + (kg >> 1));
         sl.st[j] = bf16_f32(sp[j][kg >> 5]);
       }
 #pragma unroll
@@ -158,8 +158,8 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
       const int kl = min(kb + 16 * g, kclamp), kh = min(kb + 64 + 16 * g, kclamp);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        sl.w[j][0] = ldg16_nt(wp[j] + kl);
-        sl.w[j][1] = ldg16_nt(wp[j] + kh);
+        sl.w[j][0] = ldg16(wp[j] + kl);
+        sl.w[j][1] = ldg16(wp[j] + kh);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -223,14 +223,20 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
     }
   };
 
+  // The scheduling barriers keep each refill right after the step that
+  // freed its slot: without them the scheduler sinks the loads down to their
+  // uses one round later, which leaves no load in flight while waiting.
   Slot<KIND, MB, NB> ring[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) load(ring[d], d);
+  __builtin_amdgcn_sched_barrier(0);
   for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       compute(ring[d], rd * DEPTH + d);
+      __builtin_amdgcn_sched_barrier(0);
       load(ring[d], (rd + 1) * DEPTH + d);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -369,26 +375,57 @@ struct DecodeCfg {
   int tiles, S, kc;
 };
 
-// Tile / split choice. NB grows with MB so that activation traffic (read
-// from L2) stays at or below weight traffic (streamed from HBM); the split
-// count targets >= 2048 resident waves (8 per CU) with >= DEPTH steps each.
-static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
+template <int KIND, int MB, int NB, int NWK, int DEPTH>
+static int resident_waves() {
+  // waves of this kernel that fit on the device at once (queried once)
+  static int cached = 0;
+  if (!cached) {
+    int blocks = 0, dev = 0, cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void*>(&decode_gemm_kernel<KIND, MB, NB, NWK, DEPTH>),
+            NWK * 64, 0) != hipSuccess || blocks <= 0)
+      blocks = 1;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    cached = blocks * NWK * cus;
+  }
+  return cached;
+}
+
+// Per-kind tile shape: NB grows with MB so that activation traffic (from L2)
+// stays at or below weight traffic (from HBM).
+static void decode_shape(int kind, int MB, int& NB, int& DEPTH) {
+  if (kind == kGemmW4) {
+    NB = MB >= 3 ? 2 : MB;
+    DEPTH = MB >= 3 ? 2 : (MB == 2 ? 3 : 4);
+  } else {
+    NB = MB >= 3 ? 2 : MB;
+    DEPTH = MB >= 3 ? 2 : (MB == 2 ? 3 : 4);
+  }
+}
+
+// Grid shape: 16*NB columns per workgroup, NWK waves per workgroup along K
+// and S splits of K across workgroups. The whole grid should fit in one
+// round of resident waves (a second, partly filled round costs a full wave
+// run time): take the largest NWK in {4, 2, 1} whose column tiles fit, then
+// the largest split that still fits, keeping >= 2*DEPTH steps per wave.
+// res[i] = resident waves of the NWK = 1 << i instantiation.
+static DecodeCfg decode_cfg_for(int kind, int64_t M, int64_t N, int64_t K, const int res[3]) {
   DecodeCfg c{};
   c.MB = (int)((M + 15) / 16);
-  c.NWK = 4;
-  if (kind == kGemmW4) {
-    c.NB = c.MB >= 3 ? 4 : c.MB;
-    c.DEPTH = c.MB >= 3 ? 2 : (c.MB == 2 ? 3 : 4);
-  } else {
-    c.NB = c.MB >= 3 ? 4 : c.MB;
-    c.DEPTH = c.MB >= 3 ? 2 : (c.MB == 2 ? 4 : 6);
-  }
+  decode_shape(kind, c.MB, c.NB, c.DEPTH);
   const int64_t cols = (int64_t)16 * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
+  int li = 0;
+  for (int i = 2; i >= 0; --i)
+    if ((int64_t)c.tiles * (1 << i) <= res[i] && ksteps >= (int64_t)(1 << i) * c.DEPTH) {
+      li = i;
+      break;
+    }
+  c.NWK = 1 << li;
   const int64_t waves = (int64_t)c.tiles * c.NWK;
-  int64_t S = (2048 + waves - 1) / waves;
-  S = std::min<int64_t>(S, std::max<int64_t>(1, ksteps / ((int64_t)c.NWK * c.DEPTH)));
+  int64_t S = std::max<int64_t>(1, res[li] / std::max<int64_t>(1, waves));
+  S = std::min<int64_t>(S, std::max<int64_t>(1, ksteps / ((int64_t)c.NWK * 2 * c.DEPTH)));
   S = std::max<int64_t>(1, std::min<int64_t>(S, 8));
   if (const char* e = getenv("QLIN_DECODE_SPLIT")) S = std::max(1, atoi(e));  // tuning override
   if (c.tiles > 16384) S = 1;  // counter area bound; such grids need no split
@@ -396,6 +433,50 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   c.kc = (int)(steps_per * 128);
   c.S = (int)((K + c.kc - 1) / c.kc);
   return c;
+}
+
+template <int KIND, int MB, int NB, int DEPTH>
+static DecodeCfg decode_cfg_t(int64_t M, int64_t N, int64_t K) {
+  const int res[3] = {resident_waves<KIND, MB, NB, 1, DEPTH>(), resident_waves<KIND, MB, NB, 2, DEPTH>(),
+                      resident_waves<KIND, MB, NB, 4, DEPTH>()};
+  return decode_cfg_for(KIND, M, N, K, res);
+}
+
+// Dispatch on (kind, MB) to the one instantiation that serves it.
+template <typename F>
+static auto with_decode_inst(int kind, int MB, F&& f) {
+  if (kind == kGemmW4) {
+    switch (MB) {
+      case 1: return f.template operator()<kGemmW4, 1, 1, 4>();
+      case 2: return f.template operator()<kGemmW4, 2, 2, 3>();
+      case 3: return f.template operator()<kGemmW4, 3, 2, 2>();
+      default: return f.template operator()<kGemmW4, 4, 2, 2>();
+    }
+  } else if (kind == kGemmI8) {
+    switch (MB) {
+      case 1: return f.template operator()<kGemmI8, 1, 1, 4>();
+      case 2: return f.template operator()<kGemmI8, 2, 2, 3>();
+      case 3: return f.template operator()<kGemmI8, 3, 2, 2>();
+      default: return f.template operator()<kGemmI8, 4, 2, 2>();
+    }
+  } else {
+    switch (MB) {
+      case 1: return f.template operator()<kGemmFP8, 1, 1, 4>();
+      case 2: return f.template operator()<kGemmFP8, 2, 2, 3>();
+      case 3: return f.template operator()<kGemmFP8, 3, 2, 2>();
+      default: return f.template operator()<kGemmFP8, 4, 2, 2>();
+    }
+  }
+}
+
+struct CfgFn {
+  int64_t M, N, K;
+  template <int KIND, int MB, int NB, int DEPTH>
+  DecodeCfg operator()() const { return decode_cfg_t<KIND, MB, NB, DEPTH>(M, N, K); }
+};
+
+static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
+  return with_decode_inst(kind, (int)((M + 15) / 16), CfgFn{M, N, K});
 }
 
 // Workspace of a split-K call: a fixed counter area (one word per column
@@ -411,30 +492,19 @@ size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K) {
   return kCounterBytes + round_up((size_t)c.S * M * N * 4, 256);
 }
 
-template <int KIND, int MB, int NB, int DEPTH>
-static void launch_decode_t(const GemmArgs& a, const DecodeCfg& c, hipStream_t st) {
-  decode_gemm_kernel<KIND, MB, NB, 4, DEPTH>
-      <<<dim3((unsigned)c.tiles, (unsigned)c.S), 4 * 64, 0, st>>>(a);
-}
-
-template <int KIND>
-static void launch_decode_kind(const GemmArgs& a, const DecodeCfg& c, hipStream_t st) {
-  if constexpr (KIND == kGemmW4) {
-    switch (c.MB) {
-      case 1: launch_decode_t<KIND, 1, 1, 4>(a, c, st); break;
-      case 2: launch_decode_t<KIND, 2, 2, 3>(a, c, st); break;
-      case 3: launch_decode_t<KIND, 3, 4, 2>(a, c, st); break;
-      default: launch_decode_t<KIND, 4, 4, 2>(a, c, st); break;
-    }
-  } else {
-    switch (c.MB) {
-      case 1: launch_decode_t<KIND, 1, 1, 6>(a, c, st); break;
-      case 2: launch_decode_t<KIND, 2, 2, 4>(a, c, st); break;
-      case 3: launch_decode_t<KIND, 3, 4, 2>(a, c, st); break;
-      default: launch_decode_t<KIND, 4, 4, 2>(a, c, st); break;
-    }
+struct LaunchFn {
+  const GemmArgs* a;
+  const DecodeCfg* c;
+  hipStream_t st;
+  template <int KIND, int MB, int NB, int DEPTH>
+  int operator()() const {
+    const dim3 grid((unsigned)c->tiles, (unsigned)c->S);
+    if (c->NWK == 1) decode_gemm_kernel<KIND, MB, NB, 1, DEPTH><<<grid, 64, 0, st>>>(*a);
+    else if (c->NWK == 2) decode_gemm_kernel<KIND, MB, NB, 2, DEPTH><<<grid, 2 * 64, 0, st>>>(*a);
+    else decode_gemm_kernel<KIND, MB, NB, 4, DEPTH><<<grid, 4 * 64, 0, st>>>(*a);
+    return 0;
   }
-}
+};
 
 int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const void* w,
                   const void* wsc, int64_t M, int64_t N, int64_t K, void* y, int out_f32,
@@ -458,9 +528,7 @@ int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const v
     g.cnt = reinterpret_cast<unsigned*>(ws);
     g.part = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kCounterBytes);
   }
-  if (kind == kGemmFP8) launch_decode_kind<kGemmFP8>(g, c, st);
-  else if (kind == kGemmI8) launch_decode_kind<kGemmI8>(g, c, st);
-  else launch_decode_kind<kGemmW4>(g, c, st);
+  with_decode_inst(kind, c.MB, LaunchFn{&g, &c, st});
   return launch_status();
 }
 

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
 
   // Branch-free tile fetch: rows past M / N are clamped onto the last row
   // (their outputs are never stored); K positions past K read the last valid
-  // chunk and the activation side is zeroed there, so they add nothing.
+  // chunk, and the activation side is zeroed there when the tile is stashed,
+  // so they add nothing. Nothing consumes the fetched registers before the
+  // stash, which lets the loads fly while the current tile is multiplied.
   auto fetch = [&](int kt) {
     const int kb = kt * 128;
 #pragma unroll
@@ -80,9 +82,7 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
       const int row = i / (8 * kEsz), col = i % (8 * kEsz);
       const int k = kb + col * (16 / kEsz);
       const int m = min(m0 + row, p.M - 1);
-      const uint32_t keep = k < p.K ? 0xFFFFFFFFu : 0u;
-      const uint4 v = ldg16(p.A + ((size_t)m * p.lda + min(k, p.K - 16 / kEsz)) * kEsz);
-      ra[q] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+      ra[q] = ldg16(p.A + ((size_t)m * p.lda + min(k, p.K - 16 / kEsz)) * kEsz);
     }
 #pragma unroll
     for (int q = 0; q < kWPieces; ++q) {
@@ -101,14 +101,17 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
       }
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, int kt) {
     uint8_t* la = lds[buf];
     uint8_t* lw = lds[buf] + BM * kARow;
 #pragma unroll
     for (int q = 0; q < kAPieces; ++q) {
       const int i = tid + q * NT;
       const int row = i / (8 * kEsz), col = i % (8 * kEsz);
-      *reinterpret_cast<uint4*>(la + row * kARow + col * 16) = ra[q];
+      const uint32_t keep = kt * 128 + col * (16 / kEsz) < p.K ? 0xFFFFFFFFu : 0u;
+      const uint4 v = ra[q];
+      *reinterpret_cast<uint4*>(la + row * kARow + col * 16) =
+          make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
 #pragma unroll
     for (int q = 0; q < kWPieces; ++q) {
@@ -145,14 +148,9 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
     swv[j] = KIND == kGemmW4 ? 1.0f : p.sw[min(n0 + wn * NBW * 16 + j * 16 + r, p.N - 1)];
 
   const int KT = (p.K + 127) / 128;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) fetch(kt + 1);
-    const uint8_t* la = lds[cur] + (wm * MBW * 16) * kARow;
-    const uint8_t* lw = lds[cur] + BM * kARow + (wn * NBW * 16) * kWRow;
+  auto compute = [&](int buf) {
+    const uint8_t* la = lds[buf] + (wm * MBW * 16) * kARow;
+    const uint8_t* lw = lds[buf] + BM * kARow + (wn * NBW * 16) * kWRow;
     if constexpr (KIND == kGemmW4) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {  // four 32-wide MFMA K slices
@@ -202,9 +200,20 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
           }
         }
     }
-    if (kt + 1 < KT) stash(cur ^ 1);
+  };
+
+  fetch(0);
+  stash(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    fetch(kt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kt & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stash((kt + 1) & 1, kt + 1);
     __syncthreads();
   }
+  compute((KT - 1) & 1);
 
   // ---- epilogue
 #pragma unroll

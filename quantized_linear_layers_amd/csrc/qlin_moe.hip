@@ -89,18 +89,22 @@ struct MoeGemmArgs {
 };
 
 constexpr int kMoeNW = 4;
-constexpr int kMoeDepth = 4;
-constexpr int kMoeKA = 512;
+
+__device__ __forceinline__ uint4 and4m(uint4 v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
 
 // One wave owns 16 output columns of one expert (gate_up: 16 gate rows and
-// the matching 16 up rows), the workgroup 64 columns, for up to MB*16 rows.
+// the matching 16 up rows of the bank), the workgroup 64 columns, for up to
+// MB*16 routed rows of that expert. Same streaming scheme as the dense decode
+// GEMM: weight rows (HBM) and the gathered activation rows (L2) go
+// into a DEPTH-step register ring with branch-free, clamped loads; padding
+// rows and positions past K are masked to zero on the activation side.
 template <bool GATEUP, int MB>
-__device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, int nrows,
-                                         uint8_t* lds) {
+__device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, int nrows) {
   constexpr int NB = GATEUP ? 2 : 1;
-  constexpr int kRowBytes = kMoeKA + 16;
-  constexpr int kStepsPerChunk = kMoeKA / 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int DEPTH = MB <= 1 ? 6 : (MB == 2 ? 4 : 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K;
   const int col = blockIdx.x * (kMoeNW * 16) + wave * 16 + r;  // output column of this lane
@@ -111,14 +115,17 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
   wr[0] = wbase + (size_t)colc * K;
   if (GATEUP) wr[NB - 1] = wbase + (size_t)(p.nout + colc) * K;
 
-  v4f acc[MB][NB];
+  // activation rows this lane loads (MFMA operand row r of each block)
+  const uint8_t* ap[MB];
+  uint32_t amask[MB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
-
-  // epilogue operands of this lane (row ids, token / row scales, column
-  // scales), fetched before the main loop with clamped indices
+  for (int i = 0; i < MB; ++i) {
+    const int rl = i * 16 + r;
+    const int rr = p.rows[rbeg + min(rl, nrows - 1)];
+    ap[i] = p.A + (size_t)(GATEUP ? rr / p.topk : rr) * K;
+    amask[i] = rl < nrows ? 0xFFFFFFFFu : 0u;
+  }
+  // epilogue operands (output rows 4g+q of each block, this lane's column)
   int rid[MB][4];
   float sav[MB][4];
 #pragma unroll
@@ -133,63 +140,62 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
   swv[0] = p.sw[(size_t)e * wrows + colc];
   if (GATEUP) swv[NB - 1] = p.sw[(size_t)e * wrows + p.nout + colc];
 
-  const int nsteps = (K + 127) / 128;
-  uint4 wlo[kMoeDepth][NB], whi[kMoeDepth][NB];
-  // branch-free: positions past K read the last chunk of the row; the
-  // activation side is zero there (LDS staging pads with zeros)
-  auto loadw = [&](int slot, int s) {
-    const int ka = min(s * 128 + 16 * g, K - 16), kb = min(s * 128 + 64 + 16 * g, K - 16);
+  v4f acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+
+  struct Sl {
+    uint4 w[NB][2];
+    uint4 a[MB][2];
+  };
+  const int kclamp = K - 16;
+  auto load = [&](Sl& sl, int t) {
+    const int kl = min(t * 128 + 16 * g, kclamp), kh = min(t * 128 + 64 + 16 * g, kclamp);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      wlo[slot][j] = ldg16_nt(wr[j] + ka);
-      whi[slot][j] = ldg16_nt(wr[j] + kb);
+      sl.w[j][0] = ldg16(wr[j] + kl);
+      sl.w[j][1] = ldg16(wr[j] + kh);
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      sl.a[i][0] = ldg16(ap[i] + kl);
+      sl.a[i][1] = ldg16(ap[i] + kh);
     }
   };
+  auto compute = [&](const Sl& sl, int t) {
+    const uint32_t vl = (t * 128 + 16 * g < K) ? 0xFFFFFFFFu : 0u;
+    const uint32_t vh = (t * 128 + 64 + 16 * g < K) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-  for (int d = 0; d < kMoeDepth; ++d)
-    if (d < nsteps) loadw(d, d);
-
-  for (int c0 = 0; c0 < nsteps; c0 += kStepsPerChunk) {
-    __syncthreads();
-    {
-      constexpr int kPieces = MB * 16 * (kMoeKA / 16);
-      for (int i = tid; i < kPieces; i += kMoeNW * 64) {
-        const int row = i / (kMoeKA / 16), pc = i % (kMoeKA / 16);
-        const int k = c0 * 128 + pc * 16;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < nrows && k < K) {
-          const int rr = p.rows[rbeg + row];
-          const int arow = GATEUP ? rr / p.topk : rr;
-          v = ldg16(p.A + (size_t)arow * K + k);
-        }
-        *reinterpret_cast<uint4*>(lds + row * kRowBytes + pc * 16) = v;
+    for (int i = 0; i < MB; ++i) {
+      const uint4 a0 = and4m(sl.a[i][0], amask[i] & vl);
+      const uint4 a1 = and4m(sl.a[i][1], amask[i] & vh);
+      const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint4 w0 = sl.w[j][0], w1 = sl.w[j][1];
+        const v8i wv = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
+                        (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+        acc[i][j] = mfma_fp8(av, wv, acc[i][j]);
       }
     }
-    __syncthreads();
-    const int cend = min(c0 + kStepsPerChunk, nsteps);
-    for (int s0 = c0; s0 < cend; s0 += kMoeDepth) {
+  };
+
+  const int nsteps = (K + 127) / 128;
+  const int rounds = (nsteps + DEPTH - 1) / DEPTH;
+  Sl ring[DEPTH];
 #pragma unroll
-      for (int d = 0; d < kMoeDepth; ++d) {
-        const int s = s0 + d;
-        if (s < cend) {
-          const int sl = s - c0;
+  for (int d = 0; d < DEPTH; ++d) load(ring[d], d);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
-          for (int i = 0; i < MB; ++i) {
-            const uint8_t* ap = lds + (i * 16 + r) * kRowBytes + sl * 128 + 16 * g;
-            const uint4 a0 = *reinterpret_cast<const uint4*>(ap);
-            const uint4 a1 = *reinterpret_cast<const uint4*>(ap + 64);
-            const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-              const v8i wv = {(int)wlo[d][j].x, (int)wlo[d][j].y, (int)wlo[d][j].z, (int)wlo[d][j].w,
-                              (int)whi[d][j].x, (int)whi[d][j].y, (int)whi[d][j].z, (int)whi[d][j].w};
-              acc[i][j] = mfma_fp8(av, wv, acc[i][j]);
-            }
-          }
-          if (s + kMoeDepth < nsteps) loadw(d, s + kMoeDepth);
-        }
-      }
+    for (int d = 0; d < DEPTH; ++d) {
+      compute(ring[d], rd * DEPTH + d);
+      __builtin_amdgcn_sched_barrier(0);
+      load(ring[d], (rd + 1) * DEPTH + d);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -217,16 +223,15 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
 
 template <bool GATEUP>
 __global__ __launch_bounds__(kMoeNW * 64) void moe_gemm_kernel(const MoeGemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[64 * (kMoeKA + 16)];
   const int e = blockIdx.y;
   const int beg = p.off[e], n = p.off[e + 1] - beg;
   for (int rb = 0; rb < n; rb += 64) {
     const int nr = min(64, n - rb);
     const int mb = (nr + 15) / 16;
-    if (mb == 1) moe_tile<GATEUP, 1>(p, e, beg + rb, nr, lds);
-    else if (mb == 2) moe_tile<GATEUP, 2>(p, e, beg + rb, nr, lds);
-    else if (mb == 3) moe_tile<GATEUP, 3>(p, e, beg + rb, nr, lds);
-    else moe_tile<GATEUP, 4>(p, e, beg + rb, nr, lds);
+    if (mb == 1) moe_tile<GATEUP, 1>(p, e, beg + rb, nr);
+    else if (mb == 2) moe_tile<GATEUP, 2>(p, e, beg + rb, nr);
+    else if (mb == 3) moe_tile<GATEUP, 3>(p, e, beg + rb, nr);
+    else moe_tile<GATEUP, 4>(p, e, beg + rb, nr);
   }
 }
 

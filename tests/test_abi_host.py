@@ -72,13 +72,15 @@ def test_gemm_validation(q):
 
 def test_workspace_validation(q):
     lib = q.lib()
-    need = lib.qlin_workspace_bytes(q.OP_GEMM_FP8, 64, 8192, 2048)
-    assert need > 0  # decode shape splits K across workgroups
-    assert lib.qlin_gemm_fp8(A16, A16, A16, A16, 64, 8192, 2048, A16, 0, C.c_void_p(0x100000),
+    # a narrow, deep decode shape: few column tiles, so K is split across
+    # workgroups and a workspace is needed
+    need = lib.qlin_workspace_bytes(q.OP_GEMM_FP8, 64, 512, 16384)
+    assert need > 65536
+    assert lib.qlin_gemm_fp8(A16, A16, A16, A16, 64, 512, 16384, A16, 0, C.c_void_p(0x100000),
                              need - 1, None) == q.ERR_WORKSPACE
-    assert lib.qlin_gemm_fp8(A16, A16, A16, A16, 64, 8192, 2048, A16, 0, None, need, None) == q.ERR_WORKSPACE
+    assert lib.qlin_gemm_fp8(A16, A16, A16, A16, 64, 512, 16384, A16, 0, None, need, None) == q.ERR_WORKSPACE
     # workspace must be 256-byte aligned
-    assert lib.qlin_gemm_fp8(A16, A16, A16, A16, 64, 8192, 2048, A16, 0, C.c_void_p(0x100010),
+    assert lib.qlin_gemm_fp8(A16, A16, A16, A16, 64, 512, 16384, A16, 0, C.c_void_p(0x100010),
                              need, None) == q.ERR_ALIGN
     assert lib.qlin_workspace_bytes(q.OP_GEMM_FP8, 0, 8192, 2048) == 0
     assert lib.qlin_workspace_bytes(99, 4, 512, 256) == 0
