@@ -136,17 +136,6 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-  // epilogue scales of this lane's rows / columns, fetched before the K loop
-  float sav[MBW][4], swv[NBW];
-#pragma unroll
-  for (int i = 0; i < MBW; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sav[i][e] = KIND == kGemmW4 ? 1.0f : p.sa[min(m0 + wm * MBW * 16 + i * 16 + 4 * g + e, p.M - 1)];
-#pragma unroll
-  for (int j = 0; j < NBW; ++j)
-    swv[j] = KIND == kGemmW4 ? 1.0f : p.sw[min(n0 + wn * NBW * 16 + j * 16 + r, p.N - 1)];
-
   const int KT = (p.K + 127) / 128;
   auto compute = [&](int buf) {
     const uint8_t* la = lds[buf] + (wm * MBW * 16) * kARow;
@@ -167,38 +156,46 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
           for (int j = 0; j < NBW; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
       }
     } else {
-      uint4 a0[MBW], a1[MBW], w0[NBW], w1[NBW];
-#pragma unroll
-      for (int i = 0; i < MBW; ++i) {
-        const uint8_t* ap = la + (i * 16 + r) * kARow + 16 * g;
-        a0[i] = *reinterpret_cast<const uint4*>(ap);
-        a1[i] = *reinterpret_cast<const uint4*>(ap + 64);
-      }
+      // all B fragments of the wave, then one A fragment at a time
+      uint4 w0[NBW], w1[NBW];
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
         const uint8_t* wp = lw + (j * 16 + r) * kWRow + 16 * g;
         w0[j] = *reinterpret_cast<const uint4*>(wp);
         w1[j] = *reinterpret_cast<const uint4*>(wp + 64);
       }
+      // A fragments double-buffered: the read of block i+1 is in flight while
+      // block i's MFMAs run
+      uint4 a0 = *reinterpret_cast<const uint4*>(la + r * kARow + 16 * g);
+      uint4 a1 = *reinterpret_cast<const uint4*>(la + r * kARow + 16 * g + 64);
 #pragma unroll
-      for (int i = 0; i < MBW; ++i)
+      for (int i = 0; i < MBW; ++i) {
+        uint4 n0 = a0, n1 = a1;
+        if (i + 1 < MBW) {
+          const uint8_t* ap = la + ((i + 1) * 16 + r) * kARow + 16 * g;
+          n0 = *reinterpret_cast<const uint4*>(ap);
+          n1 = *reinterpret_cast<const uint4*>(ap + 64);
+        }
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
           if constexpr (KIND == kGemmFP8) {
-            const v8i av = {(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w,
-                            (int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w};
+            const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             const v8i wv = {(int)w0[j].x, (int)w0[j].y, (int)w0[j].z, (int)w0[j].w,
                             (int)w1[j].x, (int)w1[j].y, (int)w1[j].z, (int)w1[j].w};
             acc[i][j] = mfma_fp8(av, wv, acc[i][j]);
           } else {
-            const v4i alo = {(int)a0[i].x, (int)a0[i].y, (int)a0[i].z, (int)a0[i].w};
-            const v4i ahi = {(int)a1[i].x, (int)a1[i].y, (int)a1[i].z, (int)a1[i].w};
+            const v4i alo = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
+            const v4i ahi = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
             const v4i wlo = {(int)w0[j].x, (int)w0[j].y, (int)w0[j].z, (int)w0[j].w};
             const v4i whi = {(int)w1[j].x, (int)w1[j].y, (int)w1[j].z, (int)w1[j].w};
             acc[i][j] = mfma_i8(alo, wlo, acc[i][j]);
             acc[i][j] = mfma_i8(ahi, whi, acc[i][j]);
           }
         }
+        a0 = n0;
+        a1 = n1;
+      }
     }
   };
 
@@ -215,7 +212,17 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
   }
   compute((KT - 1) & 1);
 
-  // ---- epilogue
+  // ---- epilogue: scales of this lane's rows / columns (clamped, no
+  // branches, all issued before the first use)
+  float sav[MBW][4], swv[NBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sav[i][e] = KIND == kGemmW4 ? 1.0f : p.sa[min(m0 + wm * MBW * 16 + i * 16 + 4 * g + e, p.M - 1)];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j)
+    swv[j] = KIND == kGemmW4 ? 1.0f : p.sw[min(n0 + wn * NBW * 16 + j * 16 + r, p.N - 1)];
 #pragma unroll
   for (int i = 0; i < MBW; ++i)
 #pragma unroll
@@ -256,9 +263,19 @@ int launch_prefill(int kind, const void* a, int64_t lda, const float* sa, const 
   g.K = (int)K;
   g.y = y;
   g.out_f32 = out_f32;
-  if (kind == kGemmFP8) launch_prefill_t<kGemmFP8, 128, 128, 2, 2>(g, st);
-  else if (kind == kGemmI8) launch_prefill_t<kGemmI8, 128, 128, 2, 2>(g, st);
-  else launch_prefill_t<kGemmW4, 128, 128, 2, 2>(g, st);
+  // large problems: 256x256 tiles (4 waves of 128x128: half the LDS operand
+  // traffic per flop of 64x64 wave tiles); small ones keep 128x128 tiles so
+  // the grid still fills the device
+  const bool big = M >= 1024 && N >= 1024 && (M / 256) * (N / 256) >= 256;
+  if (kind == kGemmFP8) {
+    if (big) launch_prefill_t<kGemmFP8, 256, 256, 2, 2>(g, st);
+    else launch_prefill_t<kGemmFP8, 128, 128, 2, 2>(g, st);
+  } else if (kind == kGemmI8) {
+    if (big) launch_prefill_t<kGemmI8, 256, 256, 2, 2>(g, st);
+    else launch_prefill_t<kGemmI8, 128, 128, 2, 2>(g, st);
+  } else {
+    launch_prefill_t<kGemmW4, 128, 128, 2, 2>(g, st);
+  }
   return launch_status();
 }
 
