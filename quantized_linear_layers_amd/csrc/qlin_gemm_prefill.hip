@@ -242,10 +242,276 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
       }
 }
 
+// ----------------------------------------------------------------------------
+// Large FP8 / int8 problems: persistent 256x256 tiles, software pipelined.
+//
+// One workgroup of 4 waves per CU loops over output tiles. A K stage is 128
+// bytes of K for 256 rows of A and 256 rows of W (64 KB); two stages live in
+// LDS. Each wave owns a 128x128 quadrant as 8x8 MFMA blocks and walks it in 8
+// "rows" (one A block against the 8 W blocks). While a stage is multiplied:
+//   * rows 0..6 write the next stage (already in registers) into the other
+//     LDS buffer and issue the global loads of the stage after it;
+//   * each row reads the A block of the following row;
+//   * row 7 passes the one barrier of the stage, then refills each W block
+//     register with the next stage's block right after its last MFMA.
+// Global loads: one instruction covers 8 rows x 128 contiguous bytes (whole
+// cache lines). LDS keeps every 16-row block "fragment-major": the 16-byte
+// piece that MFMA lane (g, r) needs for K half h (chunk c = 4h + g of row r)
+// sits at h*1024 + g*256 + 16*(r ^ 2c), so both the fragment reads and the
+// line-shaped staging writes hit distinct banks.
+// The MFMA takes the W block as its first operand, so each lane ends with 4
+// consecutive output columns of one row: the epilogue stores 8 (bf16) or 16
+// (fp32) bytes per lane per block. The next tile's first loads are issued
+// before the epilogue so they overlap the stores.
+// Tiles are visited in grouped order, and each round of the workgroups hands
+// every XCD a compact block of tiles (workgroups are dispatched round-robin
+// over the XCDs), so tiles that share A rows or W rows share an L2.
+template <int KIND>
+__global__ __launch_bounds__(256) void prefill_big_kernel(const PrefillArgs p, int tiles_m,
+                                                          int tiles_n) {
+  constexpr int kStage = 65536, kWOff = 32768;
+  using Acc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  __shared__ __attribute__((aligned(16))) float lds_sc[512];  // the tile's s_a rows, then s_w columns
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4, r = lane & 15;
+  const int KT = (p.K + 127) >> 7;
+  const int tiles = tiles_m * tiles_n, G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+
+  // Staging slot q (0..15) of this thread: load instruction 4q + wave, i.e.
+  // tile row srow + 32q of A (q < 8) or of W (q >= 8, row srow + 32(q-8)),
+  // 16-byte chunk c of the stage's 128 K bytes.
+  const int c = lane & 7;
+  const int srow = 8 * wave + (lane >> 3);
+  const int kofs = 16 * c;
+  const int wr_off = (wave >> 1) * 2048 + (c >> 2) * 1024 + (c & 3) * 256 + (((srow & 15) ^ (2 * c)) * 16);
+  const int rd0 = g * 256 + ((r ^ (2 * g)) * 16);
+  const int rd1 = 1024 + g * 256 + ((r ^ (2 * (4 + g))) * 16);
+  const int ra = wm * 16384, rb = kWOff + wn * 16384;
+
+  uint4 st[16];
+  v8i bf[8];  // W blocks of the current stage
+  Acc acc[8][8];
+
+  auto tile_origin = [&](int t, int& m0, int& n0) {
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (t / per_group) * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    m0 = (first_m + (t % per_group) % gsz) * 256;
+    n0 = ((t % per_group) / gsz) * 256;
+  };
+  auto gload_one = [&](int q, int kt, int m0, int n0) {
+    const int kc = min(kt * 128 + kofs, p.K - 16);
+    if (q < 8) {
+      const int m = min(m0 + srow + 32 * q, p.M - 1);
+      st[q] = ldg16(p.A + (size_t)m * p.lda + kc);
+    } else {
+      const int n = min(n0 + srow + 32 * (q - 8), p.N - 1);
+      st[q] = ldg16(p.W + (size_t)n * p.K + kc);
+    }
+  };
+  // LDS write of staging slot q (stage kt) into buffer `buf`; A chunks past K are zeroed
+  auto swrite = [&](int q, int kt, int buf) {
+    uint4 v = st[q];
+    if (q < 8) {
+      const uint32_t keep = kt * 128 + kofs < p.K ? 0xFFFFFFFFu : 0u;
+      v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    }
+    *reinterpret_cast<uint4*>(lds + buf * kStage + wr_off + 4096 * q) = v;
+  };
+  auto frag = [&](int off) {
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + off + rd0);
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + off + rd1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto mma = [&](int i, int j, const v8i& a, const v8i& w) {
+    if constexpr (KIND == kGemmFP8) {
+      acc[i][j] = mfma_fp8(w, a, acc[i][j]);
+    } else {
+      acc[i][j] = mfma_i8(__builtin_shufflevector(w, w, 0, 1, 2, 3), __builtin_shufflevector(a, a, 0, 1, 2, 3), acc[i][j]);
+      acc[i][j] = mfma_i8(__builtin_shufflevector(w, w, 4, 5, 6, 7), __builtin_shufflevector(a, a, 4, 5, 6, 7), acc[i][j]);
+    }
+  };
+
+  // The (tile, K stage) pairs of this workgroup form one stream: position
+  // pos = n*KT + kt is stage kt of its n-th tile (tile slot + n*G). The
+  // pipeline runs across tile boundaries; only the accumulators are flushed.
+  // (branch-free: a branch inside the stage body would let the compiler
+  // regroup the MFMAs away from the memory operations they hide)
+  auto stream_origin = [&](int pos, int& m0, int& n0, int& kk) {
+    const int tt = slot + (pos / KT) * G;
+    const bool live = tt < tiles;  // past the last tile: a harmless reload of valid memory
+    tile_origin(live ? tt : slot, m0, n0);
+    kk = live ? pos % KT : KT - 1;
+  };
+
+  if (slot >= tiles) return;
+  {
+    int m0, n0, kk;
+    stream_origin(0, m0, n0, kk);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) gload_one(q, kk, m0, n0);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) swrite(q, kk, 0);
+    stream_origin(1, m0, n0, kk);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) gload_one(q, kk, m0, n0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+  __syncthreads();
+  v8i af = frag(ra);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bf[j] = frag(rb + 2048 * j);
+
+  int pos = 0;
+  for (int t = slot; t < tiles; t += G) {
+    int m0, n0;
+    tile_origin(t, m0, n0);
+    for (int kt = 0; kt < KT; ++kt, ++pos) {
+      const int cur = pos & 1, nxt = cur ^ 1;
+      const int kw = (pos + 1) % KT;  // stage being written (its K tail mask)
+      int lm0, ln0, kl;               // stage being loaded
+      stream_origin(pos + 2, lm0, ln0, kl);
+      // the tile's scales go to LDS in every stage (unconditionally, see
+      // above); the epilogue reads them after the last stage's barrier
+      const float sc_a = p.sa[min(m0 + tid, p.M - 1)];
+      const float sc_w = p.sw[min(n0 + tid, p.N - 1)];
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        const v8i an = frag(cur * kStage + ra + 2048 * (i + 1));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          mma(i, j, af, bf[j]);
+          // staging slots of this row: rows 0,1 take three, rows 2..6 two
+          const int q = i < 2 ? 3 * i + (j >> 1) : 6 + 2 * (i - 2) + (j >> 2);
+          const bool here = i < 2 ? ((j & 1) && j < 6) : ((j & 3) == 1);
+          if (here) {
+            swrite(q, kw, nxt);
+            gload_one(q, kl, lm0, ln0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        af = an;
+      }
+      lds_sc[tid] = sc_a;
+      lds_sc[256 + tid] = sc_w;
+      // row 7: barrier, then the next stage's first A block and W blocks
+      mma(7, 0, af, bf[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      const v8i an = frag(nxt * kStage + ra);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j > 0) mma(7, j, af, bf[j]);
+        bf[j] = frag(nxt * kStage + rb + 2048 * j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      af = an;
+    }
+
+    // ---- epilogue. Output element (m, n) of block (i, j): lane (g, r) holds
+    // row m = .. + 16i + r, columns n = .. + 16j + 4g + e, e = 0..3.
+    // The lane index is made opaque here so that the epilogue's lane-derived
+    // offsets are computed where they are used rather than hoisted to the
+    // kernel entry (where they would only add to register pressure).
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int eg = el >> 4, er = el & 15;
+    // The next stage's fragments, loaded by the last row 7, are read again
+    // after the epilogue, so they are not live across it; scales are read
+    // from LDS where they are used.
+    auto scaled = [&](int i, int j, int e) {
+      const float sa_i = lds_sc[wm * 128 + i * 16 + er];
+      const float sw_e = lds_sc[256 + wn * 128 + j * 16 + 4 * eg + e];
+      if constexpr (KIND == kGemmI8) return ((float)acc[i][j][e] * sa_i) * sw_e;
+      else return (acc[i][j][e] * sa_i) * sw_e;
+    };
+    if (p.out_f32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + wm * 128 + i * 16 + er;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int n = n0 + wn * 128 + j * 16 + 4 * eg;
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + (size_t)m * p.N + n) =
+                make_float4(scaled(i, j, 0), scaled(i, j, 1), scaled(i, j, 2), scaled(i, j, 3));
+        }
+      }
+    } else {
+      // bf16: transpose through the LDS buffer the last stage used (free after
+      // its barrier), 32 rows of the wave's quadrant at a time, so every
+      // store writes whole 256-byte row segments. Rows are padded to 272
+      // bytes, which spreads both access shapes over the banks.
+      uint8_t* ep = lds + ((pos - 1) & 1) * kStage + wave * (32 * 272);
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = pass * 2 + ii;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = f32_bf16_rne(scaled(i, j, 0)) | (f32_bf16_rne(scaled(i, j, 1)) << 16);
+            const uint32_t hi = f32_bf16_rne(scaled(i, j, 2)) | (f32_bf16_rne(scaled(i, j, 3)) << 16);
+            *reinterpret_cast<uint2*>(ep + (ii * 16 + er) * 272 + j * 32 + eg * 8) = make_uint2(lo, hi);
+          }
+        }
+        // (LDS operations of one wave complete in order: no wait needed here)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int R = 4 * k + eg, ch = er;
+          const uint4 v = *reinterpret_cast<const uint4*>(ep + R * 272 + ch * 16);
+          const int m = m0 + wm * 128 + pass * 32 + R;
+          const int n = n0 + wn * 128 + 8 * ch;
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.N + n) = v;
+        }
+      }
+    }
+    // the next stage writes the epilogue's LDS buffer and the next scales
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+    af = frag((pos & 1) * kStage + ra);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bf[j] = frag((pos & 1) * kStage + rb + 2048 * j);
+  }
+}
+
 template <int KIND, int BM, int BN, int WM, int WN>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   prefill_gemm_kernel<KIND, BM, BN, WM, WN><<<dim3((unsigned)tiles), WM * WN * 64, 0, st>>>(a);
+}
+
+// Compute units of the current device (one persistent workgroup each).
+static int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  return cus;
+}
+
+template <int KIND>
+static void launch_prefill_big(const PrefillArgs& a, hipStream_t st) {
+  const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
+  const int grid = std::min(tm * tn, device_cus());
+  prefill_big_kernel<KIND><<<dim3((unsigned)grid), 256, 0, st>>>(a, tm, tn);
 }
 
 int launch_prefill(int kind, const void* a, int64_t lda, const float* sa, const void* w,
@@ -263,15 +529,14 @@ int launch_prefill(int kind, const void* a, int64_t lda, const float* sa, const 
   g.K = (int)K;
   g.y = y;
   g.out_f32 = out_f32;
-  // large problems: 256x256 tiles (4 waves of 128x128: half the LDS operand
-  // traffic per flop of 64x64 wave tiles); small ones keep 128x128 tiles so
-  // the grid still fills the device
-  const bool big = M >= 1024 && N >= 1024 && (M / 256) * (N / 256) >= 256;
+  // enough 256x256 tiles to occupy half the device or more: the persistent
+  // pipelined kernel; otherwise 128x128 tiles so the grid still fills it
+  const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= device_cus() / 2;
   if (kind == kGemmFP8) {
-    if (big) launch_prefill_t<kGemmFP8, 256, 256, 2, 2>(g, st);
+    if (big) launch_prefill_big<kGemmFP8>(g, st);
     else launch_prefill_t<kGemmFP8, 128, 128, 2, 2>(g, st);
   } else if (kind == kGemmI8) {
-    if (big) launch_prefill_t<kGemmI8, 256, 256, 2, 2>(g, st);
+    if (big) launch_prefill_big<kGemmI8>(g, st);
     else launch_prefill_t<kGemmI8, 128, 128, 2, 2>(g, st);
   } else {
     launch_prefill_t<kGemmW4, 128, 128, 2, 2>(g, st);

@@ -218,6 +218,8 @@ GEMM_CASES = [
     ("ragged", 1, 48, 288, (5, 17, 33, 50)),
     ("c2", 2, None, None, (1, 8, 64)),
     ("prefill_small", 1, 160, 416, (65, 130, 200)),
+    # enough 256x256 tiles for the persistent kernel, with ragged M, N and K tails
+    ("prefill_big_ragged", 1, 4112, 416, (2000,)),
 ]
 
 
