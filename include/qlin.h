@@ -204,7 +204,10 @@ int qlin_gemm_w4a16(const qlin_bf16* a, int64_t lda, const uint8_t* codes,
 
 /* FP8 linear with the per-token quantisation in front ([CARD]: activations
  * quantised to FP8 per token at run time): qlin_quant_act(QLIN_E4M3) into
- * the workspace, then qlin_gemm_fp8. x [M][lda] bf16, y [M][N] bf16. */
+ * the workspace, then qlin_gemm_fp8. x [M][lda] bf16, y [M][N] bf16.
+ * Workspace of qlin_workspace_bytes(QLIN_OP_LINEAR_*, M, N, K): the GEMM's
+ * counter area (first 64 KiB, same zero rule as above) and partial sums,
+ * then the quantised activations and their scales. */
 int qlin_linear_fp8(const qlin_bf16* x, int64_t lda, const uint8_t* w_q, const float* w_scale,
                     int64_t M, int64_t N, int64_t K, qlin_bf16* y, void* ws, size_t ws_bytes,
                     qlin_stream_t stream);

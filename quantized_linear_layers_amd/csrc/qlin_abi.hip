@@ -4,6 +4,8 @@
 #include <mutex>
 #include <string.h>
 
+#include <algorithm>
+
 #include "qlin_internal.h"
 
 namespace qlin {
@@ -157,6 +159,13 @@ static int gemm_shape_ok(int64_t M, int64_t N, int64_t K, int kmult) {
          N <= 0x7FFFFFFF && K <= 133144;
 }
 
+// A linear call keeps the GEMM's own workspace (counter area always
+// reserved, so the counters stay at offset 0 for every call) in front of
+// the quantised activations and their scales.
+static size_t linear_gemm_bytes(int kind, int64_t M, int64_t N, int64_t K) {
+  return round_up(std::max(gemm_workspace_bytes(kind, M, N, K), kGemmCounterBytes), 256);
+}
+
 size_t qlin_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   switch (op) {
@@ -164,11 +173,9 @@ size_t qlin_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     case QLIN_OP_GEMM_W8A8: return gemm_workspace_bytes(kGemmI8, M, N, K);
     case QLIN_OP_GEMM_W4A16: return gemm_workspace_bytes(kGemmW4, M, N, K);
     case QLIN_OP_LINEAR_FP8:
-      return round_up((size_t)M * K, 256) + round_up((size_t)M * 4, 256) +
-             gemm_workspace_bytes(kGemmFP8, M, N, K);
+      return linear_gemm_bytes(kGemmFP8, M, N, K) + round_up((size_t)M * K, 256) + round_up((size_t)M * 4, 256);
     case QLIN_OP_LINEAR_W8A8:
-      return round_up((size_t)M * K, 256) + round_up((size_t)M * 4, 256) +
-             gemm_workspace_bytes(kGemmI8, M, N, K);
+      return linear_gemm_bytes(kGemmI8, M, N, K) + round_up((size_t)M * K, 256) + round_up((size_t)M * 4, 256);
     default: return 0;
   }
 }
@@ -235,10 +242,10 @@ static int linear_common(int kind, const qlin_bf16* x, int64_t lda, const void* 
   QLIN_CHECK(((uintptr_t)ws & 255) == 0, QLIN_ERR_ALIGN);
   int rc = device_ok();
   if (rc) return rc;
-  uint8_t* aq = reinterpret_cast<uint8_t*>(ws);
+  uint8_t* gws = reinterpret_cast<uint8_t*>(ws);
+  const size_t gbytes = linear_gemm_bytes(kind, M, N, K);
+  uint8_t* aq = gws + gbytes;
   float* sa = reinterpret_cast<float*>(aq + round_up((size_t)M * K, 256));
-  uint8_t* gws = reinterpret_cast<uint8_t*>(sa) + round_up((size_t)M * 4, 256);
-  const size_t gbytes = ws_bytes - (size_t)(gws - aq);
   hipStream_t st = as_stream(stream);
   rc = launch_quant_act(x, M, K, lda, kind == kGemmFP8 ? QLIN_E4M3 : QLIN_INT8, aq, sa, st);
   if (rc) return rc;

@@ -11,18 +11,21 @@
 //              Y = sum_k a * bf16(c * step)
 //
 // At M <= 64 the layer is bound by streaming the weights from HBM. Design:
-//  * a workgroup of NWK waves owns 16*NB output columns and one K range;
-//    its waves take consecutive slices of the range (split-K across
-//    workgroups as well when the grid would otherwise be too small);
-//  * each wave streams its 16*NB weight rows (16-byte loads) and
-//    its activation rows (L2-resident) into registers, DEPTH 128-wide K steps
-//    ahead of use, with branch-free loads;
-//  * MFMA with M padded to 16 (padding rows masked to zero);
+//  * a workgroup of 4 waves owns 64*NB output columns (16*NB per wave) and
+//    one K range (split-K across workgroups when the column tiles alone
+//    would not fill the device);
+//  * the activations of the K range pass through LDS in chunks of 256 K,
+//    double buffered and shared by the 4 waves (one barrier per chunk), so
+//    each activation byte is fetched once per workgroup, in whole cache
+//    lines, and MFMA fragments come from LDS;
+//  * each wave streams its own weight rows into a ring of DEPTH 128-K steps
+//    of registers, DEPTH steps ahead of use, with branch-free clamped loads;
+//  * MFMA with M padded to 16 (padding rows are zero in LDS);
 //  * the int4 unpack and every scale are fused into the kernel;
-//  * wave partial sums meet in LDS in wave order; split-K partial sums go to
-//    the workspace and the last workgroup of a column tile to arrive (device-
-//    scope counter) sums them in split order, so results are deterministic,
-//    applies the epilogue and resets the counter.
+//  * split-K partial sums go to the workspace and the last workgroup of a
+//    column tile to arrive (device-scope counter) sums them in split order,
+//    so results are deterministic; it applies the epilogue and resets the
+//    counter.
 #include <stdlib.h>
 
 #include <algorithm>
@@ -41,73 +44,59 @@ struct GemmArgs {
   const uint16_t* steps;  // W4A16: bf16 [N][K/32]
   const float* sw;        // [N] (fp8 / int8)
   int M, N, K;
-  int kc;                 // K per split, multiple of 128
+  int kc;                 // K per split, multiple of 256
   void* y;
   int out_f32;
   uint32_t* part;         // [S][M][N] fp32 / int32 partial sums
   unsigned* cnt;          // one arrival counter per column tile
 };
 
-// One 128-wide K step of one wave: the weight fragments of its NB 16-row
-// blocks and the activation fragments of its MB 16-row blocks.
+// One 128-wide K step of one wave's weight rows.
 //   fp8 / int8: lane (r, g) holds row r, bytes [16g, 16g+16) and
-//               [64+16g, 80+16g) of the step (same K order for both
-//               operands, as the MFMA requires).
+//               [64+16g, 80+16g) of the step.
 //   W4A16:      lane (r, g) holds row r, the 32 codes of group g (16 bytes)
-//               and its step; activations k = 32g + 8w + [0, 8), w = 0..3.
-template <int KIND, int MB, int NB>
-struct Slot;
-template <int MB, int NB>
-struct Slot<kGemmFP8, MB, NB> {
+//               and the group's step.
+template <int KIND, int NB>
+struct Slot {
   uint4 w[NB][2];
-  uint4 a[MB][2];
 };
-template <int MB, int NB>
-struct Slot<kGemmI8, MB, NB> {
-  uint4 w[NB][2];
-  uint4 a[MB][2];
-};
-template <int MB, int NB>
-struct Slot<kGemmW4, MB, NB> {
+template <int NB>
+struct Slot<kGemmW4, NB> {
   uint4 w[NB];
   float st[NB];
-  uint4 a[MB][4];
 };
 
-__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) {
-  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-}
-
-// Decode-shaped GEMM. A workgroup of NWK waves owns 16*NB output columns and
-// one K range (split-K across workgroups); its waves take consecutive slices
-// of that range. Each wave streams its weight rows and activation rows into
-// registers DEPTH steps ahead of use: loads never depend on a branch (out of
-// range addresses are clamped onto data the wave reads anyway, and the
-// activation fragment is masked to zero instead), so the steady-state loop is
-// straight-line code with DEPTH steps of loads in flight. Partial sums of the
-// waves meet in LDS (fixed order); split-K partial sums meet in the workspace
-// (fixed order, last arriving workgroup of the tile).
-template <int KIND, int MB, int NB, int NWK, int DEPTH>
-__global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p) {
+// Decode-shaped GEMM, see the file comment. LDS layout of one activation
+// chunk: for each 16-row block mb and 128-K step s, a "fragment-major" block
+// in which the 16 bytes that MFMA lane (r, g) reads for one operand piece sit
+// at piece*1024 + g*256 + 16*(r ^ f(chunk)); the XOR spreads the line-shaped
+// staging writes over the banks as well.
+//   fp8 / int8 (2 KB per block): piece = K half h; chunk c = 4h + g (16-byte
+//     chunk of the 128-byte step), f = 2c.
+//   bf16 (4 KB per block): piece = MFMA w of the step; chunk c = 4g + w (the
+//     8 values k = 32g + 8w .. +8), f = c.
+template <int KIND, int MB, int NB, int DEPTH>
+__global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
+  static_assert(DEPTH % 4 == 0, "a round holds an even number of 2-step chunks");
   using Acc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
-  constexpr int kAccWords = MB * NB * 4;
-  __shared__ __attribute__((aligned(16))) uint32_t red[(NWK > 1 ? NWK - 1 : 1) * 64 * kAccWords];
+  constexpr int ESZ = KIND == kGemmW4 ? 2 : 1;       // activation bytes per element
+  constexpr int kBlk = 16 * 128 * ESZ;               // LDS bytes per (mb, step)
+  constexpr int kBuf = MB * 2 * kBlk;                // one 256-K chunk
+  constexpr int kRowPieces = 16 * ESZ;               // 16-byte pieces per row per chunk
+  constexpr int kPer = MB * 16 * kRowPieces / 256;   // pieces per thread per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+  __shared__ unsigned last_flag;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int S = gridDim.y, split = blockIdx.y;
-  const int k0 = split * p.kc;
-  const int kend = min(k0 + p.kc, p.K);
-  const int nsteps = (kend - k0 + 127) >> 7;
-  const int spw = (nsteps + NWK - 1) / NWK;
-  const int sb = min(wave * spw, nsteps), se = min(sb + spw, nsteps);
-  const int kw0 = k0 + sb * 128;
-  const int kw1 = min(kend, k0 + se * 128);  // this wave's K range [kw0, kw1)
-  const int rounds = (se - sb + DEPTH - 1) / DEPTH;
-  constexpr int kChunk = KIND == kGemmW4 ? 32 : 16;  // load granule along K
-  const int kclamp = max(kw1 - kChunk, 0);
-  const int n0 = blockIdx.x * 16 * NB;
+  const int split = blockIdx.y, S = gridDim.y;
+  const int k0 = split * p.kc, k1 = min(k0 + p.kc, p.K);
+  const int nsteps = (k1 - k0 + 127) >> 7;
+  const int rounds = (nsteps + DEPTH - 1) / DEPTH;
+  const int n0 = (blockIdx.x * 4 + wave) * 16 * NB;  // this wave's first column
 
+  // ---- weight rows of this wave (clamped: rows past N repeat the last one)
   const uint8_t* wp[NB];
   const uint16_t* sp[NB];
 #pragma unroll
@@ -121,17 +110,64 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
       sp[j] = nullptr;
     }
   }
-  const uint8_t* ap[MB];
-  uint32_t amask[MB];
+  constexpr int kChunk = KIND == kGemmW4 ? 32 : 16;  // weight load granule along K
+  const int kclamp = max(k1 - kChunk, 0);
+  auto wload = [&](Slot<KIND, NB>& sl, int t) {
+    const int kb = k0 + t * 128;
+    if constexpr (KIND == kGemmW4) {
+      const int kg = min(kb + 32 * g, kclamp);
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int row = mb * 16 + r;
-    ap[mb] = p.A + (size_t)min(row, p.M - 1) * p.lda * (KIND == kGemmW4 ? 2 : 1);
-    amask[mb] = row < p.M ? 0xFFFFFFFFu : 0u;
-  }
+      for (int j = 0; j < NB; ++j) {
+        sl.w[j] = ldg16(wp[j] + (kg >> 1));
+        sl.st[j] = bf16_f32(sp[j][kg >> 5]);
+      }
+    } else {
+      const int kl = min(kb + 16 * g, kclamp), kh = min(kb + 64 + 16 * g, kclamp);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        sl.w[j][0] = ldg16(wp[j] + kl);
+        sl.w[j][1] = ldg16(wp[j] + kh);
+      }
+    }
+  };
 
-  // epilogue scales of this lane's rows / columns, fetched up front (clamped
-  // addresses, no branches) so that their latency hides under the main loop
+  // ---- activation chunks: piece q of this thread is row (tid + 256q) / kRowPieces.
+  // Loads are clamped and stay unmasked in registers (masking them at load
+  // time would make the next instruction wait for every load in flight);
+  // rows past M and K past the range are zeroed when written to LDS.
+  uint4 aset[2][kPer];
+  auto aload = [&](int ci, uint4 (&dst)[kPer]) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int pc = tid + 256 * q;
+      const int row = pc / kRowPieces, piece = pc % kRowPieces;
+      const int k = k0 + ci * 256 + piece * (16 / ESZ);
+      dst[q] = ldg16(p.A + ((size_t)min(row, p.M - 1) * p.lda + min(k, p.K - 16 / ESZ)) * ESZ);
+    }
+  };
+  auto awrite = [&](const uint4 (&src)[kPer], int ci, int buf) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int pc = tid + 256 * q;
+      const int row = pc / kRowPieces, piece = pc % kRowPieces;
+      const int k = k0 + ci * 256 + piece * (16 / ESZ);
+      const uint32_t m = row < p.M && k < k1 ? 0xFFFFFFFFu : 0u;
+      const int mb = row >> 4, rr = row & 15;
+      const int s = piece / (8 * ESZ), c = piece % (8 * ESZ);
+      int off;
+      if constexpr (KIND == kGemmW4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
+      else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ (2 * c)) & 15) * 16;
+      const uint4 v = src[q];
+      *reinterpret_cast<uint4*>(lds + buf * kBuf + (mb * 2 + s) * kBlk + off) =
+          make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+    }
+  };
+  // lane offsets of the fragment reads
+  const int rd0 = g * 256 + ((r ^ (2 * g)) & 15) * 16;
+  const int rd1 = 1024 + g * 256 + ((r ^ (2 * (4 + g))) & 15) * 16;
+  const int rdw = g * 256;  // bf16: + w*1024 + ((r ^ (4g + w)) & 15) * 16
+
+  // epilogue scales of this lane's rows / columns, fetched up front
   float sav[MB][4], swv[NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -141,44 +177,15 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
 #pragma unroll
   for (int j = 0; j < NB; ++j) swv[j] = KIND == kGemmW4 ? 1.0f : p.sw[min(n0 + 16 * j + r, p.N - 1)];
 
-  auto load = [&](Slot<KIND, MB, NB>& sl, int t) {
-    const int kb = kw0 + t * 128;
-    if constexpr (KIND == kGemmW4) {
-      const int kg = min(kb + 32 * g, kclamp);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        sl.w[j] = ldg16(wp[j] + (kg >> 1));
-        sl.st[j] = bf16_f32(sp[j][kg >> 5]);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) sl.a[mb][w] = ldg16(ap[mb] + (size_t)(kg + 8 * w) * 2);
-    } else {
-      const int kl = min(kb + 16 * g, kclamp), kh = min(kb + 64 + 16 * g, kclamp);
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        sl.w[j][0] = ldg16(wp[j] + kl);
-        sl.w[j][1] = ldg16(wp[j] + kh);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        sl.a[mb][0] = ldg16(ap[mb] + kl);
-        sl.a[mb][1] = ldg16(ap[mb] + kh);
-      }
-    }
-  };
-
   Acc acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
 
-  auto compute = [&](const Slot<KIND, MB, NB>& sl, int t) {
-    const int kb = kw0 + t * 128;
+  auto compute = [&](const Slot<KIND, NB>& sl, int t) {
+    const uint8_t* base = lds + ((t >> 1) & 1) * kBuf + (t & 1) * kBlk;
     if constexpr (KIND == kGemmW4) {
-      const uint32_t vg = (kb + 32 * g < kw1) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         v8bf bf[NB];
@@ -187,111 +194,88 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
           const uint32_t cw = w == 0 ? sl.w[j].x : w == 1 ? sl.w[j].y : w == 2 ? sl.w[j].z : sl.w[j].w;
           bf[j] = dequant8(cw, sl.st[j], -8.0f * sl.st[j]);
         }
+        const int off = w * 1024 + rdw + ((r ^ (4 * g + w)) & 15) * 16;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const v8bf af = __builtin_bit_cast(v8bf, and4(sl.a[mb][w], amask[mb] & vg));
+          const v8bf af = *reinterpret_cast<const v8bf*>(base + mb * 2 * kBlk + off);
 #pragma unroll
           for (int j = 0; j < NB; ++j) acc[mb][j] = mfma_bf16(af, bf[j], acc[mb][j]);
         }
       }
     } else {
-      const uint32_t vl = (kb + 16 * g < kw1) ? 0xFFFFFFFFu : 0u;
-      const uint32_t vh = (kb + 64 + 16 * g < kw1) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const uint4 a0 = and4(sl.a[mb][0], amask[mb] & vl);
-        const uint4 a1 = and4(sl.a[mb][1], amask[mb] & vh);
+        const v4i a0 = *reinterpret_cast<const v4i*>(base + mb * 2 * kBlk + rd0);
+        const v4i a1 = *reinterpret_cast<const v4i*>(base + mb * 2 * kBlk + rd1);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const uint4 w0 = sl.w[j][0], w1 = sl.w[j][1];
+          const v4i wlo = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
+          const v4i whi = {(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
           if constexpr (KIND == kGemmFP8) {
-            const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            const v8i wv = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
-                            (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-            acc[mb][j] = mfma_fp8(av, wv, acc[mb][j]);
+            acc[mb][j] = mfma_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                  __builtin_shufflevector(wlo, whi, 0, 1, 2, 3, 4, 5, 6, 7), acc[mb][j]);
           } else {
-            const v4i alo = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
-            const v4i ahi = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            const v4i wlo = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
-            const v4i whi = {(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-            acc[mb][j] = mfma_i8(alo, wlo, acc[mb][j]);
-            acc[mb][j] = mfma_i8(ahi, whi, acc[mb][j]);
+            acc[mb][j] = mfma_i8(a0, wlo, acc[mb][j]);
+            acc[mb][j] = mfma_i8(a1, whi, acc[mb][j]);
           }
         }
       }
     }
   };
 
-  // The scheduling barriers keep each refill right after the step that
-  // freed its slot: without them the scheduler sinks the loads down to their
-  // uses one round later, which leaves no load in flight while waiting.
-  Slot<KIND, MB, NB> ring[DEPTH];
+  // ---- prologue: activation chunks 0 and 1 in registers, chunk 0 in LDS,
+  // the weight ring filled
+  aload(0, aset[0]);
+  aload(1, aset[1]);
+  Slot<KIND, NB> ring[DEPTH];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load(ring[d], d);
-  __builtin_amdgcn_sched_barrier(0);
+  for (int d = 0; d < DEPTH; ++d) wload(ring[d], d);
+  awrite(aset[0], 0, 0);
+  __syncthreads();
+
+  // ---- main loop: DEPTH steps (DEPTH/2 chunks) per round. Chunk ci uses LDS
+  // buffer ci & 1 and register set ci & 1; at its start the set is refilled
+  // with chunk ci + 2, at its end chunk ci + 1 goes to the other buffer.
+  // Steps past the range multiply zero activations (clamped weight loads).
+  // The scheduling barriers keep each refill right after the step that
+  // freed its slot.
   for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      compute(ring[d], rd * DEPTH + d);
+      const int t = rd * DEPTH + d;
+      if ((d & 1) == 0) aload((t >> 1) + 2, aset[(d >> 1) & 1]);
+      compute(ring[d], t);
       __builtin_amdgcn_sched_barrier(0);
-      load(ring[d], (rd + 1) * DEPTH + d);
+      wload(ring[d], t + DEPTH);
       __builtin_amdgcn_sched_barrier(0);
+      if (d & 1) {
+        awrite(aset[((d >> 1) + 1) & 1], (t >> 1) + 1, ((t >> 1) + 1) & 1);
+        __syncthreads();
+      }
     }
   }
 
-  // ---- waves of the workgroup meet in LDS, summed in wave order by wave 0
+  // ---- split-K: publish partials, the last workgroup of the tile reduces
   float accf[MB][NB][4];
+  int acci[MB][NB][4];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) accf[mb][j][i] = 0.0f;
-  int acci[MB][NB][4];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const Acc v = acc[mb][j];
-#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if constexpr (KIND == kGemmI8) acci[mb][j][i] = v[i];
-        else accf[mb][j][i] = v[i];
+        accf[mb][j][i] = 0.0f;
+        acci[mb][j][i] = 0;
+        if constexpr (KIND == kGemmI8) acci[mb][j][i] = acc[mb][j][i];
+        else accf[mb][j][i] = acc[mb][j][i];
       }
-    }
-  if constexpr (NWK > 1) {
-    if (wave > 0) {
-      uint32_t* dst = red + (size_t)(wave - 1) * 64 * kAccWords;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = (mb * NB + j) * 4 + i;
-            dst[e * 64 + lane] = KIND == kGemmI8 ? (uint32_t)acci[mb][j][i]
-                                                 : __float_as_uint(accf[mb][j][i]);
-          }
-    }
-    __syncthreads();
-    if (wave > 0) return;
-    for (int w = 1; w < NWK; ++w) {
-      const uint32_t* src = red + (size_t)(w - 1) * 64 * kAccWords;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t u = src[((mb * NB + j) * 4 + i) * 64 + lane];
-            if constexpr (KIND == kGemmI8) acci[mb][j][i] += (int)u;
-            else accf[mb][j][i] = accf[mb][j][i] + __uint_as_float(u);
-          }
-    }
-  }
-
-  // ---- split-K: publish partials, the last workgroup of the tile reduces
+  // Partial sums and the counter use device-scope relaxed atomic accesses,
+  // which bypass the per-XCD L2 caches; a store is complete (vmcnt) once it
+  // is visible device-wide, so waiting for the stores before the counter
+  // increment orders them without a cache-wide write-back fence (a fence
+  // here would flush and invalidate the whole L2 of the XCD on every
+  // workgroup).
   if (S > 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -301,15 +285,17 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
         for (int i = 0; i < 4; ++i) {
           const int m = mb * 16 + 4 * g + i, n = n0 + 16 * j + r;
           if (m < p.M && n < p.N)
-            p.part[((size_t)split * p.M + m) * p.N + n] =
-                KIND == kGemmI8 ? (uint32_t)acci[mb][j][i] : __float_as_uint(accf[mb][j][i]);
+            __hip_atomic_store(&p.part[((size_t)split * p.M + m) * p.N + n],
+                               KIND == kGemmI8 ? (uint32_t)acci[mb][j][i] : __float_as_uint(accf[mb][j][i]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-    __threadfence();
-    unsigned old = 0;
-    if (lane == 0) old = atomicAdd(&p.cnt[blockIdx.x], 1u);
-    old = __shfl(old, 0, kWave);
-    if (old != (unsigned)(S - 1)) return;
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial sums are visible
+    __syncthreads();                // ... and those of the other waves
+    if (tid == 0)
+      last_flag = __hip_atomic_fetch_add(&p.cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (unsigned)(S - 1);
+    __syncthreads();
+    if (!last_flag) return;
     // sum the splits in split order; every load of one split is issued
     // before the first is consumed (clamped addresses, no branches)
     const size_t stride = (size_t)p.M * p.N;
@@ -328,27 +314,27 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t u = p.part[off[mb][j][i]];
+          const uint32_t u = __hip_atomic_load(&p.part[off[mb][j][i]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if constexpr (KIND == kGemmI8) acci[mb][j][i] = (int)u;
           else accf[mb][j][i] = __uint_as_float(u);
         }
     for (int s = 1; s < S; ++s) {
-      const uint32_t* q = p.part + (size_t)s * stride;
+      uint32_t* q = p.part + (size_t)s * stride;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const uint32_t u = q[off[mb][j][i]];
+            const uint32_t u = __hip_atomic_load(&q[off[mb][j][i]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if constexpr (KIND == kGemmI8) acci[mb][j][i] += (int)u;
             else accf[mb][j][i] = accf[mb][j][i] + __uint_as_float(u);
           }
     }
-    if (lane == 0) p.cnt[blockIdx.x] = 0u;
+    if (tid == 0) __hip_atomic_store(&p.cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- epilogue (wave 0 of the workgroup)
+  // ---- epilogue
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -371,120 +357,79 @@ __global__ __launch_bounds__(NWK * 64) void decode_gemm_kernel(const GemmArgs p)
 // launch configuration
 // ----------------------------------------------------------------------------
 struct DecodeCfg {
-  int MB, NB, NWK, DEPTH;
+  int MB, NB, DEPTH;
   int tiles, S, kc;
 };
 
-template <int KIND, int MB, int NB, int NWK, int DEPTH>
-static int resident_waves() {
-  // waves of this kernel that fit on the device at once (queried once)
-  static int cached = 0;
-  if (!cached) {
-    int blocks = 0, dev = 0, cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, reinterpret_cast<const void*>(&decode_gemm_kernel<KIND, MB, NB, NWK, DEPTH>),
-            NWK * 64, 0) != hipSuccess || blocks <= 0)
-      blocks = 1;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    cached = blocks * NWK * cus;
-  }
-  return cached;
+// Compute units of the current device (queried once).
+static int decode_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  return cus;
 }
 
-// Per-kind tile shape: NB grows with MB so that activation traffic (from L2)
-// stays at or below weight traffic (from HBM).
-static void decode_shape(int kind, int MB, int& NB, int& DEPTH) {
-  if (kind == kGemmW4) {
-    NB = MB >= 3 ? 2 : MB;
-    DEPTH = MB >= 3 ? 2 : (MB == 2 ? 3 : 4);
-  } else {
-    NB = MB >= 3 ? 2 : MB;
-    DEPTH = MB >= 3 ? 2 : (MB == 2 ? 3 : 4);
-  }
+// Per-kind tile shape: a wave takes two column blocks once the activation
+// fragments it reads per weight byte would otherwise dominate (MB >= 3).
+static int decode_nb(int kind, int MB) {
+  if (kind == kGemmW4) return MB >= 2 ? 2 : 1;
+  return MB >= 3 ? 2 : 1;
 }
 
-// Grid shape: 16*NB columns per workgroup, NWK waves per workgroup along K
-// and S splits of K across workgroups. The whole grid should fit in one
-// round of resident waves (a second, partly filled round costs a full wave
-// run time): take the largest NWK in {4, 2, 1} whose column tiles fit, then
-// the largest split that still fits, keeping >= 2*DEPTH steps per wave.
-// res[i] = resident waves of the NWK = 1 << i instantiation.
-static DecodeCfg decode_cfg_for(int kind, int64_t M, int64_t N, int64_t K, const int res[3]) {
+// Grid: 64*NB columns per workgroup, S splits of K. Split-K costs a write
+// and a read of S*M*N partial sums, so it is used only to reach about three
+// quarters of the CUs with column tiles; each split keeps >= 4 steps. DEPTH
+// is 8 when the split's step count is a multiple of 8 or large, else 4 (a
+// round computes DEPTH steps; extra steps are harmless but cost time).
+static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   c.MB = (int)((M + 15) / 16);
-  decode_shape(kind, c.MB, c.NB, c.DEPTH);
-  const int64_t cols = (int64_t)16 * c.NB;
+  c.NB = decode_nb(kind, c.MB);
+  const int64_t cols = (int64_t)64 * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
-  int li = 0;
-  for (int i = 2; i >= 0; --i)
-    if ((int64_t)c.tiles * (1 << i) <= res[i] && ksteps >= (int64_t)(1 << i) * c.DEPTH) {
-      li = i;
-      break;
-    }
-  c.NWK = 1 << li;
-  const int64_t waves = (int64_t)c.tiles * c.NWK;
-  int64_t S = std::max<int64_t>(1, res[li] / std::max<int64_t>(1, waves));
-  S = std::min<int64_t>(S, std::max<int64_t>(1, ksteps / ((int64_t)c.NWK * 2 * c.DEPTH)));
-  S = std::max<int64_t>(1, std::min<int64_t>(S, 8));
+  const int64_t want = 3 * (int64_t)decode_cus() / 4;
+  int64_t S = (want + c.tiles - 1) / c.tiles;
+  S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
   if (const char* e = getenv("QLIN_DECODE_SPLIT")) S = std::max(1, atoi(e));  // tuning override
   if (c.tiles > 16384) S = 1;  // counter area bound; such grids need no split
-  const int64_t steps_per = (ksteps + S - 1) / S;
+  int64_t steps_per = (ksteps + S - 1) / S;
+  steps_per = (steps_per + 1) / 2 * 2;  // whole 256-K chunks
   c.kc = (int)(steps_per * 128);
   c.S = (int)((K + c.kc - 1) / c.kc);
+  c.DEPTH = (steps_per % 8 == 0 || steps_per > 24) ? 8 : 4;
   return c;
 }
 
-template <int KIND, int MB, int NB, int DEPTH>
-static DecodeCfg decode_cfg_t(int64_t M, int64_t N, int64_t K) {
-  const int res[3] = {resident_waves<KIND, MB, NB, 1, DEPTH>(), resident_waves<KIND, MB, NB, 2, DEPTH>(),
-                      resident_waves<KIND, MB, NB, 4, DEPTH>()};
-  return decode_cfg_for(KIND, M, N, K, res);
-}
-
-// Dispatch on (kind, MB) to the one instantiation that serves it.
+// Dispatch on (kind, MB, DEPTH) to the instantiation that serves it.
 template <typename F>
-static auto with_decode_inst(int kind, int MB, F&& f) {
-  if (kind == kGemmW4) {
-    switch (MB) {
-      case 1: return f.template operator()<kGemmW4, 1, 1, 4>();
-      case 2: return f.template operator()<kGemmW4, 2, 2, 3>();
-      case 3: return f.template operator()<kGemmW4, 3, 2, 2>();
-      default: return f.template operator()<kGemmW4, 4, 2, 2>();
-    }
-  } else if (kind == kGemmI8) {
-    switch (MB) {
-      case 1: return f.template operator()<kGemmI8, 1, 1, 4>();
-      case 2: return f.template operator()<kGemmI8, 2, 2, 3>();
-      case 3: return f.template operator()<kGemmI8, 3, 2, 2>();
-      default: return f.template operator()<kGemmI8, 4, 2, 2>();
-    }
-  } else {
-    switch (MB) {
-      case 1: return f.template operator()<kGemmFP8, 1, 1, 4>();
-      case 2: return f.template operator()<kGemmFP8, 2, 2, 3>();
-      case 3: return f.template operator()<kGemmFP8, 3, 2, 2>();
-      default: return f.template operator()<kGemmFP8, 4, 2, 2>();
-    }
+static auto with_decode_inst(int kind, int MB, int DEPTH, F&& f) {
+#define QLIN_DEC_MB(K, NB1, NB2)                                              \
+  switch (MB) {                                                               \
+    case 1: return DEPTH == 8 ? f.template operator()<K, 1, NB1, 8>() : f.template operator()<K, 1, NB1, 4>(); \
+    case 2: return DEPTH == 8 ? f.template operator()<K, 2, NB2, 8>() : f.template operator()<K, 2, NB2, 4>(); \
+    case 3: return f.template operator()<K, 3, 2, 4>();                       \
+    default: return f.template operator()<K, 4, 2, 4>();                      \
   }
-}
-
-struct CfgFn {
-  int64_t M, N, K;
-  template <int KIND, int MB, int NB, int DEPTH>
-  DecodeCfg operator()() const { return decode_cfg_t<KIND, MB, NB, DEPTH>(M, N, K); }
-};
-
-static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
-  return with_decode_inst(kind, (int)((M + 15) / 16), CfgFn{M, N, K});
+  if (kind == kGemmW4) {
+    QLIN_DEC_MB(kGemmW4, 1, 2)
+  } else if (kind == kGemmI8) {
+    QLIN_DEC_MB(kGemmI8, 1, 1)
+  } else {
+    QLIN_DEC_MB(kGemmFP8, 1, 1)
+  }
+#undef QLIN_DEC_MB
 }
 
 // Workspace of a split-K call: a fixed counter area (one word per column
 // tile, at most kMaxTiles) at offset 0, then the partial sums. Every call
 // leaves the counter area zero, and no call ever writes partials there, so a
 // workspace zeroed once stays valid across calls of any shape.
-constexpr int kMaxTiles = 16384;
-constexpr size_t kCounterBytes = (size_t)kMaxTiles * 4;
+constexpr size_t kCounterBytes = kGemmCounterBytes;
+constexpr int kMaxTiles = (int)(kCounterBytes / 4);
 
 size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K) {
   const DecodeCfg c = decode_cfg(kind, M, N, K);
@@ -498,10 +443,7 @@ struct LaunchFn {
   hipStream_t st;
   template <int KIND, int MB, int NB, int DEPTH>
   int operator()() const {
-    const dim3 grid((unsigned)c->tiles, (unsigned)c->S);
-    if (c->NWK == 1) decode_gemm_kernel<KIND, MB, NB, 1, DEPTH><<<grid, 64, 0, st>>>(*a);
-    else if (c->NWK == 2) decode_gemm_kernel<KIND, MB, NB, 2, DEPTH><<<grid, 2 * 64, 0, st>>>(*a);
-    else decode_gemm_kernel<KIND, MB, NB, 4, DEPTH><<<grid, 4 * 64, 0, st>>>(*a);
+    decode_gemm_kernel<KIND, MB, NB, DEPTH><<<dim3((unsigned)c->tiles, (unsigned)c->S), 256, 0, st>>>(*a);
     return 0;
   }
 };
@@ -528,7 +470,7 @@ int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const v
     g.cnt = reinterpret_cast<unsigned*>(ws);
     g.part = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kCounterBytes);
   }
-  with_decode_inst(kind, c.MB, LaunchFn{&g, &c, st});
+  with_decode_inst(kind, c.MB, c.DEPTH, LaunchFn{&g, &c, st});
   return launch_status();
 }
 

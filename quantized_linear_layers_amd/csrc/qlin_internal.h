@@ -46,6 +46,9 @@ int launch_fp8_encode(const float* x, int64_t n, int fmt, uint8_t* out, hipStrea
 // ---- GEMMs (qlin_gemm_decode.hip, qlin_gemm_prefill.hip)
 enum GemmKind { kGemmFP8 = 0, kGemmI8 = 1, kGemmW4 = 2 };
 size_t gemm_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K);
+// Split-K arrival counters occupy the first kGemmCounterBytes of every GEMM
+// workspace (zero between calls); partial sums follow them.
+constexpr size_t kGemmCounterBytes = 65536;
 int launch_gemm(int kind, const void* a, int64_t lda, const float* sa, const void* w,
                 const void* wsc, int64_t M, int64_t N, int64_t K, void* y, int out_f32, void* ws,
                 size_t ws_bytes, hipStream_t st);
