@@ -51,40 +51,47 @@ struct GemmArgs {
   unsigned* cnt;          // one arrival counter per column tile
 };
 
-// One 128-wide K step of one wave's weight rows.
-//   fp8 / int8: lane (r, g) holds row r, bytes [16g, 16g+16) and
-//               [64+16g, 80+16g) of the step.
-//   W4A16:      lane (r, g) holds row r, the 32 codes of group g (16 bytes)
-//               and the group's step.
+// One "unit" of one wave's weight rows: 16 rows x 128 bytes per 16-row block
+// (128 K of fp8/int8, 256 K of int4 codes), fetched as two line-shaped
+// loads (lane l: row 8h + l/8, 16-byte chunk l%8) and held in registers
+// until it is written to the wave's LDS slot; W4A16 adds the 8 group steps
+// of each row (lane l: row l/4, groups 2(l%4) and 2(l%4)+1).
 template <int KIND, int NB>
 struct Slot {
   uint4 w[NB][2];
 };
 template <int NB>
 struct Slot<kGemmW4, NB> {
-  uint4 w[NB];
-  float st[NB];
+  uint4 w[NB][2];
+  uint32_t st[NB][2];
 };
 
-// Decode-shaped GEMM, see the file comment. LDS layout of one activation
-// chunk: for each 16-row block mb and 128-K step s, a "fragment-major" block
-// in which the 16 bytes that MFMA lane (r, g) reads for one operand piece sit
-// at piece*1024 + g*256 + 16*(r ^ f(chunk)); the XOR spreads the line-shaped
-// staging writes over the banks as well.
-//   fp8 / int8 (2 KB per block): piece = K half h; chunk c = 4h + g (16-byte
-//     chunk of the 128-byte step), f = 2c.
-//   bf16 (4 KB per block): piece = MFMA w of the step; chunk c = 4g + w (the
-//     8 values k = 32g + 8w .. +8), f = c.
+// Decode-shaped GEMM, see the file comment. Both operands reach the MFMAs
+// from LDS in a "fragment-major" layout: the 16 bytes that MFMA lane (r, g)
+// reads for one operand piece sit at piece*1024 + g*256 + 16*(r ^ f(c)),
+// where c is the 16-byte chunk of the row segment; the XOR spreads the
+// line-shaped staging writes over the banks.
+//   fp8 / int8 (2 KB per 16-row block and 128-K step): piece = K half h,
+//     chunk c = 4h + g, f = 2c. Weights use the same layout.
+//   int4 weights (2 KB per block and unit of two steps): piece = step s,
+//     chunk c = 4s + g (the 32 codes of group 4s + g), f = 2c.
+//   bf16 activations (4 KB per block and step): piece = MFMA w of the step,
+//     chunk c = 4g + w (the 8 values k = 32g + 8w .. +8), f = c.
 template <int KIND, int MB, int NB, int DEPTH>
 __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
-  static_assert(DEPTH % 4 == 0, "a round holds an even number of 2-step chunks");
   using Acc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
-  constexpr int ESZ = KIND == kGemmW4 ? 2 : 1;       // activation bytes per element
-  constexpr int kBlk = 16 * 128 * ESZ;               // LDS bytes per (mb, step)
-  constexpr int kBuf = MB * 2 * kBlk;                // one 256-K chunk
+  constexpr bool W4 = KIND == kGemmW4;
+  constexpr int ESZ = W4 ? 2 : 1;                    // activation bytes per element
+  constexpr int kUnitK = W4 ? 256 : 128;             // K per weight unit
+  constexpr int UPC = 256 / kUnitK;                  // units per activation chunk
+  static_assert(DEPTH % (2 * UPC) == 0, "a round holds an even number of chunks");
+  constexpr int kBlk = 16 * 128 * ESZ;               // LDS bytes per (mb, step) of activations
+  constexpr int kBuf = MB * 2 * kBlk;                // one 256-K activation chunk
   constexpr int kRowPieces = 16 * ESZ;               // 16-byte pieces per row per chunk
-  constexpr int kPer = MB * 16 * kRowPieces / 256;   // pieces per thread per chunk
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+  constexpr int kPer = MB * 16 * kRowPieces / 256;   // activation pieces per thread per chunk
+  constexpr int kWSlot = NB * 2048;                  // one wave's weight unit in LDS
+  constexpr int kSSlot = W4 ? NB * 256 : 0;          // ... and its int4 group steps
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf + 4 * (kWSlot + kSSlot)];
   __shared__ unsigned last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -92,42 +99,56 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   const int r = lane & 15, g = lane >> 4;
   const int split = blockIdx.y, S = gridDim.y;
   const int k0 = split * p.kc, k1 = min(k0 + p.kc, p.K);
-  const int nsteps = (k1 - k0 + 127) >> 7;
-  const int rounds = (nsteps + DEPTH - 1) / DEPTH;
+  const int nunits = (k1 - k0 + kUnitK - 1) / kUnitK;
+  const int rounds = (nunits + DEPTH - 1) / DEPTH;
   const int n0 = (blockIdx.x * 4 + wave) * 16 * NB;  // this wave's first column
+  uint8_t* wslot = lds + 2 * kBuf + wave * kWSlot;
+  uint8_t* sslot = lds + 2 * kBuf + 4 * kWSlot + wave * kSSlot;
 
   // ---- weight rows of this wave (clamped: rows past N repeat the last one)
-  const uint8_t* wp[NB];
+  const int wc = lane & 7;  // 16-byte chunk of a line-shaped load
+  const uint8_t* wp[NB][2];
   const uint16_t* sp[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int row = min(n0 + 16 * j + r, p.N - 1);
-    if constexpr (KIND == kGemmW4) {
-      wp[j] = p.W + (size_t)row * (p.K / 2);
-      sp[j] = p.steps + (size_t)row * (p.K / 32);
-    } else {
-      wp[j] = p.W + (size_t)row * p.K;
-      sp[j] = nullptr;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = min(n0 + 16 * j + 8 * h + (lane >> 3), p.N - 1);
+      wp[j][h] = p.W + (size_t)row * (W4 ? p.K / 2 : p.K) + 16 * wc;
     }
+    sp[j] = W4 ? p.steps + (size_t)min(n0 + 16 * j + (lane >> 2), p.N - 1) * (p.K / 32) : nullptr;
   }
-  constexpr int kChunk = KIND == kGemmW4 ? 32 : 16;  // weight load granule along K
-  const int kclamp = max(k1 - kChunk, 0);
-  auto wload = [&](Slot<KIND, NB>& sl, int t) {
-    const int kb = k0 + t * 128;
-    if constexpr (KIND == kGemmW4) {
-      const int kg = min(kb + 32 * g, kclamp);
+  // last valid byte offset of a 16-byte chunk within the range, and group
+  const int bclamp = (W4 ? k1 / 2 : k1) - 16 - 16 * wc;
+  const int gmax = k1 / 32 - 1;
+  auto wload = [&](Slot<KIND, NB>& sl, int u) {
+    const int kb = k0 + u * kUnitK;
+    const int bo = min(W4 ? kb / 2 : kb, bclamp);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        sl.w[j] = ldg16(wp[j] + (kg >> 1));
-        sl.st[j] = bf16_f32(sp[j][kg >> 5]);
+    for (int j = 0; j < NB; ++j) {
+      sl.w[j][0] = ldg16_nt(wp[j][0] + bo);
+      sl.w[j][1] = ldg16_nt(wp[j][1] + bo);
+      if constexpr (W4) {
+        const int gi = kb / 32 + 2 * (lane & 3);
+        sl.st[j][0] = sp[j][min(gi, gmax)];
+        sl.st[j][1] = sp[j][min(gi + 1, gmax)];
       }
-    } else {
-      const int kl = min(kb + 16 * g, kclamp), kh = min(kb + 64 + 16 * g, kclamp);
+    }
+  };
+  // weight unit -> this wave's LDS slot (wave-private: LDS operations of one
+  // wave complete in order, so no barrier is needed before reading it back)
+  const int wr = (wc >> 2) * 1024 + (wc & 3) * 256;
+  auto wstage = [&](const Slot<KIND, NB>& sl) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        sl.w[j][0] = ldg16(wp[j] + kl);
-        sl.w[j][1] = ldg16(wp[j] + kh);
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int R = 8 * h + (lane >> 3);
+        *reinterpret_cast<uint4*>(wslot + j * 2048 + wr + ((R ^ (2 * wc)) & 15) * 16) = sl.w[j][h];
       }
+      if constexpr (W4)
+        *reinterpret_cast<uint32_t*>(sslot + j * 256 + (lane >> 2) * 16 + (lane & 3) * 4) =
+            (sl.st[j][0] & 0xFFFFu) | (sl.st[j][1] << 16);
     }
   };
 
@@ -155,7 +176,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
       const int mb = row >> 4, rr = row & 15;
       const int s = piece / (8 * ESZ), c = piece % (8 * ESZ);
       int off;
-      if constexpr (KIND == kGemmW4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
+      if constexpr (W4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
       else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ (2 * c)) & 15) * 16;
       const uint4 v = src[q];
       *reinterpret_cast<uint4*>(lds + buf * kBuf + (mb * 2 + s) * kBlk + off) =
@@ -173,9 +194,9 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      sav[mb][i] = KIND == kGemmW4 ? 1.0f : p.sa[min(mb * 16 + 4 * g + i, p.M - 1)];
+      sav[mb][i] = W4 ? 1.0f : p.sa[min(mb * 16 + 4 * g + i, p.M - 1)];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) swv[j] = KIND == kGemmW4 ? 1.0f : p.sw[min(n0 + 16 * j + r, p.N - 1)];
+  for (int j = 0; j < NB; ++j) swv[j] = W4 ? 1.0f : p.sw[min(n0 + 16 * j + r, p.N - 1)];
 
   Acc acc[MB][NB];
 #pragma unroll
@@ -183,41 +204,58 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
 
-  auto compute = [&](const Slot<KIND, NB>& sl, int t) {
-    const uint8_t* base = lds + ((t >> 1) & 1) * kBuf + (t & 1) * kBlk;
-    if constexpr (KIND == kGemmW4) {
+  // multiply the weight unit in the wave's slot (unit u) with the
+  // activation chunk that holds it
+  auto compute = [&](int u) {
+    const uint8_t* abase = lds + ((u / UPC) & 1) * kBuf;
+    if constexpr (W4) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        v8bf bf[NB];
+      for (int s = 0; s < 2; ++s) {
+        uint4 cw[NB];
+        float st[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const uint32_t cw = w == 0 ? sl.w[j].x : w == 1 ? sl.w[j].y : w == 2 ? sl.w[j].z : sl.w[j].w;
-          bf[j] = dequant8(cw, sl.st[j], -8.0f * sl.st[j]);
+          cw[j] = *reinterpret_cast<const uint4*>(wslot + j * 2048 + s * 1024 + g * 256 +
+                                                  ((r ^ (2 * (4 * s + g))) & 15) * 16);
+          st[j] = bf16_f32(*reinterpret_cast<const uint16_t*>(sslot + j * 256 + r * 16 + (4 * s + g) * 2));
         }
-        const int off = w * 1024 + rdw + ((r ^ (4 * g + w)) & 15) * 16;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const v8bf af = *reinterpret_cast<const v8bf*>(base + mb * 2 * kBlk + off);
+        for (int w = 0; w < 4; ++w) {
+          v8bf bf[NB];
 #pragma unroll
-          for (int j = 0; j < NB; ++j) acc[mb][j] = mfma_bf16(af, bf[j], acc[mb][j]);
+          for (int j = 0; j < NB; ++j) {
+            const uint32_t word = w == 0 ? cw[j].x : w == 1 ? cw[j].y : w == 2 ? cw[j].z : cw[j].w;
+            bf[j] = dequant8(word, st[j], -8.0f * st[j]);
+          }
+          const int off = s * kBlk + w * 1024 + rdw + ((r ^ (4 * g + w)) & 15) * 16;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const v8bf af = *reinterpret_cast<const v8bf*>(abase + mb * 2 * kBlk + off);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[mb][j] = mfma_bf16(af, bf[j], acc[mb][j]);
+          }
         }
       }
     } else {
+      const uint8_t* ab = abase + (u & 1) * kBlk;
+      v4i w0[NB], w1[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        w0[j] = *reinterpret_cast<const v4i*>(wslot + j * 2048 + rd0);
+        w1[j] = *reinterpret_cast<const v4i*>(wslot + j * 2048 + rd1);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const v4i a0 = *reinterpret_cast<const v4i*>(base + mb * 2 * kBlk + rd0);
-        const v4i a1 = *reinterpret_cast<const v4i*>(base + mb * 2 * kBlk + rd1);
+        const v4i a0 = *reinterpret_cast<const v4i*>(ab + mb * 2 * kBlk + rd0);
+        const v4i a1 = *reinterpret_cast<const v4i*>(ab + mb * 2 * kBlk + rd1);
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          const uint4 w0 = sl.w[j][0], w1 = sl.w[j][1];
-          const v4i wlo = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w};
-          const v4i whi = {(int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
           if constexpr (KIND == kGemmFP8) {
             acc[mb][j] = mfma_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                  __builtin_shufflevector(wlo, whi, 0, 1, 2, 3, 4, 5, 6, 7), acc[mb][j]);
+                                  __builtin_shufflevector(w0[j], w1[j], 0, 1, 2, 3, 4, 5, 6, 7), acc[mb][j]);
           } else {
-            acc[mb][j] = mfma_i8(a0, wlo, acc[mb][j]);
-            acc[mb][j] = mfma_i8(a1, whi, acc[mb][j]);
+            acc[mb][j] = mfma_i8(a0, w0[j], acc[mb][j]);
+            acc[mb][j] = mfma_i8(a1, w1[j], acc[mb][j]);
           }
         }
       }
@@ -234,23 +272,25 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   awrite(aset[0], 0, 0);
   __syncthreads();
 
-  // ---- main loop: DEPTH steps (DEPTH/2 chunks) per round. Chunk ci uses LDS
+  // ---- main loop: DEPTH units per round. Activation chunk ci uses LDS
   // buffer ci & 1 and register set ci & 1; at its start the set is refilled
-  // with chunk ci + 2, at its end chunk ci + 1 goes to the other buffer.
-  // Steps past the range multiply zero activations (clamped weight loads).
-  // The scheduling barriers keep each refill right after the step that
-  // freed its slot.
+  // with chunk ci + 2, after its last unit chunk ci + 1 goes to the other
+  // buffer. Each unit: its registers go to the wave's slot, the ring slot is
+  // refilled DEPTH units ahead, then the unit is multiplied. Units past the
+  // range multiply zero activations (clamped weight loads). The scheduling
+  // barriers keep each refill right after the write that freed its slot.
   for (int rd = 0; rd < rounds; ++rd) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-      const int t = rd * DEPTH + d;
-      if ((d & 1) == 0) aload((t >> 1) + 2, aset[(d >> 1) & 1]);
-      compute(ring[d], t);
+      const int u = rd * DEPTH + d;
+      if (d % UPC == 0) aload(u / UPC + 2, aset[(d / UPC) & 1]);
+      wstage(ring[d]);
       __builtin_amdgcn_sched_barrier(0);
-      wload(ring[d], t + DEPTH);
+      wload(ring[d], u + DEPTH);
       __builtin_amdgcn_sched_barrier(0);
-      if (d & 1) {
-        awrite(aset[((d >> 1) + 1) & 1], (t >> 1) + 1, ((t >> 1) + 1) & 1);
+      compute(u);
+      if (d % UPC == UPC - 1) {
+        awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
         __syncthreads();
       }
     }
@@ -381,9 +421,10 @@ static int decode_nb(int kind, int MB) {
 
 // Grid: 64*NB columns per workgroup, S splits of K. Split-K costs a write
 // and a read of S*M*N partial sums, so it is used only to reach about three
-// quarters of the CUs with column tiles; each split keeps >= 4 steps. DEPTH
-// is 8 when the split's step count is a multiple of 8 or large, else 4 (a
-// round computes DEPTH steps; extra steps are harmless but cost time).
+// quarters of the CUs with column tiles; each split keeps >= 4 steps of
+// 128 K. DEPTH (weight units in flight per wave) is the larger choice when
+// the split's unit count is a multiple of it or large (a round computes
+// DEPTH units; extra units are harmless but cost time).
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   c.MB = (int)((M + 15) / 16);
@@ -395,33 +436,37 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   int64_t S = (want + c.tiles - 1) / c.tiles;
   S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
   if (const char* e = getenv("QLIN_DECODE_SPLIT")) S = std::max(1, atoi(e));  // tuning override
-  if (c.tiles > 16384) S = 1;  // counter area bound; such grids need no split
+  if (c.tiles > (int)(kGemmCounterBytes / 4)) S = 1;  // one counter per tile; such grids need no split
   int64_t steps_per = (ksteps + S - 1) / S;
   steps_per = (steps_per + 1) / 2 * 2;  // whole 256-K chunks
   c.kc = (int)(steps_per * 128);
   c.S = (int)((K + c.kc - 1) / c.kc);
-  c.DEPTH = (steps_per % 8 == 0 || steps_per > 24) ? 8 : 4;
+  const int64_t units = kind == kGemmW4 ? steps_per / 2 : steps_per;
+  const int big = kind == kGemmW4 ? 4 : 8;
+  c.DEPTH = (c.MB <= 2 && (units % big == 0 || units > 3 * big)) ? big : big / 2;
   return c;
 }
 
 // Dispatch on (kind, MB, DEPTH) to the instantiation that serves it.
 template <typename F>
 static auto with_decode_inst(int kind, int MB, int DEPTH, F&& f) {
-#define QLIN_DEC_MB(K, NB1, NB2)                                              \
-  switch (MB) {                                                               \
-    case 1: return DEPTH == 8 ? f.template operator()<K, 1, NB1, 8>() : f.template operator()<K, 1, NB1, 4>(); \
-    case 2: return DEPTH == 8 ? f.template operator()<K, 2, NB2, 8>() : f.template operator()<K, 2, NB2, 4>(); \
-    case 3: return f.template operator()<K, 3, 2, 4>();                       \
-    default: return f.template operator()<K, 4, 2, 4>();                      \
+#define QLIN_DEC(K, NB1, NB2, D)                                                        \
+  switch (MB) {                                                                          \
+    case 1: return DEPTH == 2 * D ? f.template operator()<K, 1, NB1, 2 * D>()            \
+                                  : f.template operator()<K, 1, NB1, D>();               \
+    case 2: return DEPTH == 2 * D ? f.template operator()<K, 2, NB2, 2 * D>()            \
+                                  : f.template operator()<K, 2, NB2, D>();               \
+    case 3: return f.template operator()<K, 3, 2, D>();                                  \
+    default: return f.template operator()<K, 4, 2, D>();                                 \
   }
   if (kind == kGemmW4) {
-    QLIN_DEC_MB(kGemmW4, 1, 2)
+    QLIN_DEC(kGemmW4, 1, 2, 2)
   } else if (kind == kGemmI8) {
-    QLIN_DEC_MB(kGemmI8, 1, 1)
+    QLIN_DEC(kGemmI8, 1, 1, 4)
   } else {
-    QLIN_DEC_MB(kGemmFP8, 1, 1)
+    QLIN_DEC(kGemmFP8, 1, 1, 4)
   }
-#undef QLIN_DEC_MB
+#undef QLIN_DEC
 }
 
 // Workspace of a split-K call: a fixed counter area (one word per column
@@ -429,7 +474,6 @@ static auto with_decode_inst(int kind, int MB, int DEPTH, F&& f) {
 // leaves the counter area zero, and no call ever writes partials there, so a
 // workspace zeroed once stays valid across calls of any shape.
 constexpr size_t kCounterBytes = kGemmCounterBytes;
-constexpr int kMaxTiles = (int)(kCounterBytes / 4);
 
 size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K) {
   const DecodeCfg c = decode_cfg(kind, M, N, K);
