@@ -16,6 +16,7 @@
 // Experts that no token routes to are never read.
 #include "qlin_device.h"
 #include "qlin_internal.h"
+#include "qlin_skinny.h"
 
 namespace qlin {
 
@@ -88,44 +89,45 @@ struct MoeGemmArgs {
   float* out;          // act [R][I] or d [R][H]
 };
 
-constexpr int kMoeNW = 4;
-
-__device__ __forceinline__ uint4 and4m(uint4 v, uint32_t m) {
-  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-}
-
-// One wave owns 16 output columns of one expert (gate_up: 16 gate rows and
-// the matching 16 up rows of the bank), the workgroup 64 columns, for up to
-// MB*16 routed rows of that expert. Same streaming scheme as the dense decode
-// GEMM: weight rows (HBM) and the gathered activation rows (L2) go
-// into a DEPTH-step register ring with branch-free, clamped loads; padding
-// rows and positions past K are masked to zero on the activation side.
+// One workgroup: 64 output columns of one expert (gate_up: 64 gate
+// columns and the matching 64 up columns of the bank), for up to MB*16 of
+// the expert's routed rows at a time; the weights stream once per row block
+// through the skinny GEMM core (qlin_skinny.h), gathered activation rows
+// pass through LDS.
 template <bool GATEUP, int MB>
-__device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, int nrows) {
+__device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int e, int rbeg, int nrows) {
   constexpr int NB = GATEUP ? 2 : 1;
-  constexpr int DEPTH = MB <= 1 ? 6 : (MB == 2 ? 4 : 2);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int DEPTH = (GATEUP || MB > 2) ? 4 : 8;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K;
-  const int col = blockIdx.x * (kMoeNW * 16) + wave * 16 + r;  // output column of this lane
-  const int colc = min(col, p.nout - 1);
+  const int c0 = blockIdx.x * 64 + wave * 16;  // this wave's first output column
   const size_t wrows = GATEUP ? 2 * (size_t)p.nout : (size_t)p.nout;
   const uint8_t* wbase = p.W + (size_t)e * wrows * K;
-  const uint8_t* wr[NB];
-  wr[0] = wbase + (size_t)colc * K;
-  if (GATEUP) wr[NB - 1] = wbase + (size_t)(p.nout + colc) * K;
 
-  // activation rows this lane loads (MFMA operand row r of each block)
-  const uint8_t* ap[MB];
-  uint32_t amask[MB];
+  const uint8_t* wp[NB][2];
+  const uint16_t* sp[NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int rl = i * 16 + r;
-    const int rr = p.rows[rbeg + min(rl, nrows - 1)];
-    ap[i] = p.A + (size_t)(GATEUP ? rr / p.topk : rr) * K;
-    amask[i] = rl < nrows ? 0xFFFFFFFFu : 0u;
+  for (int j = 0; j < NB; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = min(c0 + 8 * h + (lane >> 3), p.nout - 1);
+      wp[j][h] = wbase + (size_t)(j * p.nout + col) * K + 16 * (lane & 7);
+    }
+    sp[j] = nullptr;
+  }
+  const uint8_t* ap[MB];
+  uint32_t am[MB];
+#pragma unroll
+  for (int q = 0; q < MB; ++q) {
+    const int i = (tid + 256 * q) / 16;  // tile row of this thread's chunk piece
+    const int rr = p.rows[rbeg + min(i, nrows - 1)];
+    ap[q] = p.A + (size_t)(GATEUP ? rr / p.topk : rr) * K;
+    am[q] = i < nrows ? 0xFFFFFFFFu : 0u;
   }
   // epilogue operands (output rows 4g+q of each block, this lane's column)
+  const int col = c0 + r, colc = min(col, p.nout - 1);
   int rid[MB][4];
   float sav[MB][4];
 #pragma unroll
@@ -145,61 +147,8 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+  skinny_mma<kGemmFP8, MB, NB, DEPTH>(lds, wp, sp, ap, am, K, 0, K, acc);
 
-  struct Sl {
-    uint4 w[NB][2];
-    uint4 a[MB][2];
-  };
-  const int kclamp = K - 16;
-  auto load = [&](Sl& sl, int t) {
-    const int kl = min(t * 128 + 16 * g, kclamp), kh = min(t * 128 + 64 + 16 * g, kclamp);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      sl.w[j][0] = ldg16(wr[j] + kl);
-      sl.w[j][1] = ldg16(wr[j] + kh);
-    }
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      sl.a[i][0] = ldg16(ap[i] + kl);
-      sl.a[i][1] = ldg16(ap[i] + kh);
-    }
-  };
-  auto compute = [&](const Sl& sl, int t) {
-    const uint32_t vl = (t * 128 + 16 * g < K) ? 0xFFFFFFFFu : 0u;
-    const uint32_t vh = (t * 128 + 64 + 16 * g < K) ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      const uint4 a0 = and4m(sl.a[i][0], amask[i] & vl);
-      const uint4 a1 = and4m(sl.a[i][1], amask[i] & vh);
-      const v8i av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const uint4 w0 = sl.w[j][0], w1 = sl.w[j][1];
-        const v8i wv = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
-                        (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-        acc[i][j] = mfma_fp8(av, wv, acc[i][j]);
-      }
-    }
-  };
-
-  const int nsteps = (K + 127) / 128;
-  const int rounds = (nsteps + DEPTH - 1) / DEPTH;
-  Sl ring[DEPTH];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load(ring[d], d);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int rd = 0; rd < rounds; ++rd) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      compute(ring[d], rd * DEPTH + d);
-      __builtin_amdgcn_sched_barrier(0);
-      load(ring[d], (rd + 1) * DEPTH + d);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // epilogue: lane holds rows 4g+q of each block, column `col`
   if (col < p.nout) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -219,36 +168,58 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, int e, int rbeg, 
         }
       }
   }
+  __syncthreads();  // the next row block reuses the LDS
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(kMoeNW * 64) void moe_gemm_kernel(const MoeGemmArgs p) {
+// Row blocks of up to 64 rows; the LARGE instantiation serves blocks of 33..64
+// rows, the other one blocks of 1..32 rows, so that the common small blocks
+// do not pay the registers (and occupancy) of the large ones. Workgroups
+// with nothing to do return at once.
+template <bool GATEUP, bool LARGE>
+__global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeGemmArgs p) {
+  constexpr int NB = GATEUP ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<kGemmFP8, LARGE ? 4 : 2, NB>()];
   const int e = blockIdx.y;
   const int beg = p.off[e], n = p.off[e + 1] - beg;
   for (int rb = 0; rb < n; rb += 64) {
     const int nr = min(64, n - rb);
     const int mb = (nr + 15) / 16;
-    if (mb == 1) moe_tile<GATEUP, 1>(p, e, beg + rb, nr);
-    else if (mb == 2) moe_tile<GATEUP, 2>(p, e, beg + rb, nr);
-    else if (mb == 3) moe_tile<GATEUP, 3>(p, e, beg + rb, nr);
-    else moe_tile<GATEUP, 4>(p, e, beg + rb, nr);
+    if constexpr (LARGE) {
+      if (mb == 3) moe_tile<GATEUP, 3>(p, lds, e, beg + rb, nr);
+      else if (mb == 4) moe_tile<GATEUP, 4>(p, lds, e, beg + rb, nr);
+    } else {
+      if (mb == 1) moe_tile<GATEUP, 1>(p, lds, e, beg + rb, nr);
+      else if (mb == 2) moe_tile<GATEUP, 2>(p, lds, e, beg + rb, nr);
+    }
   }
 }
 
 // ---------------------------------------------------------------- combine
+// y[t][h] = bf16(sum_j p[t][j] * d[t*topk + j][h]), j ascending; slots with
+// an expert id outside [0, E) contribute nothing. One thread per (t, 4 h).
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ d,
                                                           const int32_t* __restrict__ ids,
-                                                          const float* __restrict__ wts, int topk,
+                                                          const float* __restrict__ wts, int T, int topk,
                                                           int H, int E, uint16_t* __restrict__ y) {
-  const int t = blockIdx.x;
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    float acc = 0.0f;
-    for (int j = 0; j < topk; ++j) {
-      const int e = ids[t * topk + j];
-      if (e >= 0 && e < E) acc = acc + wts[t * topk + j] * d[((size_t)t * topk + j) * H + h];
+  const int hq = H / 4;
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)T * hq) return;
+  const int t = (int)(i / hq), h = (int)(i % hq) * 4;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  for (int j = 0; j < topk; ++j) {
+    const int e = ids[t * topk + j];
+    const float w = (e >= 0 && e < E) ? wts[t * topk + j] : 0.0f;
+    const float4 v = *reinterpret_cast<const float4*>(d + ((size_t)t * topk + j) * H + h);
+    if (e >= 0 && e < E) {
+      a0 = a0 + w * v.x;
+      a1 = a1 + w * v.y;
+      a2 = a2 + w * v.z;
+      a3 = a3 + w * v.w;
     }
-    y[(size_t)t * H + h] = (uint16_t)f32_bf16_rne(acc);
   }
+  const uint32_t lo = f32_bf16_rne(a0) | (f32_bf16_rne(a1) << 16);
+  const uint32_t hi = f32_bf16_rne(a2) | (f32_bf16_rne(a3) << 16);
+  *reinterpret_cast<uint2*>(y + (size_t)t * H + h) = make_uint2(lo, hi);
 }
 
 int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
@@ -271,17 +242,26 @@ int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E
   moe_route_kernel<<<1, 1024, 2 * E * sizeof(int), st>>>(ids, R, (int)E, off, rows);
   if ((rc = launch_status())) return rc;
 
+  // every expert's rows fit one small block when T*topk/E is small; the
+  // large-block launches are skipped when no expert can reach 33 rows
+  const bool any_large = R > 32;
   MoeGemmArgs gu{xq, sx, w13, s13, off, rows, topk, (int)H, (int)I, act};
-  moe_gemm_kernel<true><<<dim3((unsigned)((I + 63) / 64), (unsigned)E), kMoeNW * 64, 0, st>>>(gu);
+  const dim3 ggrid((unsigned)((I + 63) / 64), (unsigned)E);
+  moe_gemm_kernel<true, false><<<ggrid, 256, 0, st>>>(gu);
+  if (any_large) moe_gemm_kernel<true, true><<<ggrid, 256, 0, st>>>(gu);
   if ((rc = launch_status())) return rc;
 
   if ((rc = launch_quant_rows_f32(act, R, I, aq, sa, st))) return rc;
 
   MoeGemmArgs dn{aq, sa, w2, s2, off, rows, topk, (int)I, (int)H, dd};
-  moe_gemm_kernel<false><<<dim3((unsigned)((H + 63) / 64), (unsigned)E), kMoeNW * 64, 0, st>>>(dn);
+  const dim3 dgrid((unsigned)((H + 63) / 64), (unsigned)E);
+  moe_gemm_kernel<false, false><<<dgrid, 256, 0, st>>>(dn);
+  if (any_large) moe_gemm_kernel<false, true><<<dgrid, 256, 0, st>>>(dn);
   if ((rc = launch_status())) return rc;
 
-  moe_combine_kernel<<<dim3((unsigned)T), 256, 0, st>>>(dd, ids, wts, topk, (int)H, (int)E, y);
+  const long long threads = T * (H / 4);
+  moe_combine_kernel<<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(dd, ids, wts, (int)T, topk,
+                                                                             (int)H, (int)E, y);
   return launch_status();
 }
 

@@ -1,0 +1,267 @@
+// Streaming core of the weight-bound ("skinny", M <= 64 rows) quantized
+// GEMMs of libqlin: the dense decode GEMMs and the MoE expert GEMMs.
+//
+// A workgroup of 4 waves computes an (MB*16) x (4 * NB*16) output tile over
+// one K range [k0, k1):
+//  * activations pass through LDS in chunks of 256 K, double buffered and
+//    shared by the 4 waves (one barrier per chunk), fetched once per
+//    workgroup in whole cache lines; rows past the valid count and K past
+//    the range are zeroed when written;
+//  * each wave streams its own 16*NB weight rows in "units" (16 rows x 128
+//    bytes per 16-row block: 128 K of fp8/int8, 256 K of int4 codes) with
+//    line-shaped nontemporal loads (8 rows x 128 B per instruction), DEPTH
+//    units ahead of use, and writes each unit to a wave-private LDS slot
+//    from which the MFMA fragments are read (LDS operations of one wave
+//    complete in order, so that slot needs no barrier);
+//  * LDS blocks are "fragment-major": the 16 bytes that MFMA lane (r, g)
+//    reads for one operand piece sit at piece*1024 + g*256 + 16*(r ^ f(c)),
+//    c being the 16-byte chunk of the row segment; the XOR spreads the
+//    line-shaped staging writes over the banks.
+//      fp8 / int8 (2 KB per 16-row block and 128-K step): piece = K half h,
+//        chunk c = 4h + g, f = 2c; weights use the same layout;
+//      int4 weights (2 KB per block and unit of two steps): piece = step s,
+//        chunk c = 4s + g (the 32 codes of group 4s + g), f = 2c;
+//      bf16 activations (4 KB per block and step): piece = MFMA w of the
+//        step, chunk c = 4g + w (values k = 32g + 8w .. +8), f = c.
+//  * the int4 unpack (bf16(c * step), exact product, one rounding) happens
+//    right before the MFMAs.
+// Output layout (MFMA): acc[mb][j] register i of lane (r, g) is row
+// mb*16 + 4g + i, column 16j + r of the wave's columns.
+#pragma once
+
+#include <type_traits>
+
+#include "qlin_device.h"
+#include "qlin_internal.h"
+
+namespace qlin {
+
+template <int KIND>
+using SkinnyAcc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
+
+// Per-workgroup LDS bytes of skinny_mma<KIND, MB, NB>.
+template <int KIND, int MB, int NB>
+constexpr int skinny_lds_bytes() {
+  return 2 * MB * 2 * 16 * 128 * (KIND == kGemmW4 ? 2 : 1) + 4 * NB * (2048 + (KIND == kGemmW4 ? 256 : 0));
+}
+
+// One weight unit of one wave in registers.
+template <int KIND, int NB>
+struct SkinnySlot {
+  uint4 w[NB][2];
+};
+template <int NB>
+struct SkinnySlot<kGemmW4, NB> {
+  uint4 w[NB][2];
+  uint32_t st[NB][2];
+};
+
+// Inputs of one tile, per lane:
+//  wp[j][h]  weight row of block j, tile row 8h + lane/8, already offset by
+//            16 * (lane % 8) bytes (clamped onto a valid row);
+//  sp[j]     int4 group steps of tile row lane/4 of block j (W4A16 only);
+//  wbytes    weight bytes per row (K or K/2);
+//  ap[q]     activation row of this thread's chunk piece q (row
+//            (tid + 256q) / (16 * ESZ) of the tile; clamped onto a valid row)
+//  am[q]     0xFFFFFFFF if that row is a real row, else 0;
+//  K         full K (clamps the activation loads), k0/k1 the range.
+template <int KIND, int MB, int NB, int DEPTH>
+__device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB][2], const uint16_t* (&sp)[NB],
+                                           const uint8_t* (&ap)[MB * (KIND == kGemmW4 ? 2 : 1)],
+                                           uint32_t (&am)[MB * (KIND == kGemmW4 ? 2 : 1)], int K, int k0,
+                                           int k1, SkinnyAcc<KIND> (&acc)[MB][NB]) {
+  constexpr bool W4 = KIND == kGemmW4;
+  constexpr int ESZ = W4 ? 2 : 1;                    // activation bytes per element
+  constexpr int kUnitK = W4 ? 256 : 128;             // K per weight unit
+  constexpr int UPC = 256 / kUnitK;                  // units per activation chunk
+  static_assert(DEPTH % (2 * UPC) == 0, "a round holds an even number of chunks");
+  constexpr int kBlk = 16 * 128 * ESZ;               // LDS bytes per (mb, step) of activations
+  constexpr int kBuf = MB * 2 * kBlk;                // one 256-K activation chunk
+  constexpr int kRowPieces = 16 * ESZ;               // 16-byte pieces per row per chunk
+  constexpr int kPer = MB * ESZ;                     // activation pieces per thread per chunk
+  constexpr int kWSlot = NB * 2048;                  // one wave's weight unit in LDS
+  constexpr int kSSlot = W4 ? NB * 256 : 0;          // ... and its int4 group steps
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int nunits = (k1 - k0 + kUnitK - 1) / kUnitK;
+  uint8_t* wslot = lds + 2 * kBuf + wave * kWSlot;
+  uint8_t* sslot = lds + 2 * kBuf + 4 * kWSlot + wave * kSSlot;
+
+  // ---- weights
+  const int wc = lane & 7;
+  const int bclamp = (W4 ? k1 / 2 : k1) - 16 - 16 * wc;
+  const int gmax = k1 / 32 - 1;
+  auto wload = [&](SkinnySlot<KIND, NB>& sl, int u) {
+    const int kb = k0 + u * kUnitK;
+    const int bo = min(W4 ? kb / 2 : kb, bclamp);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      sl.w[j][0] = ldg16_nt(wp[j][0] + bo);
+      sl.w[j][1] = ldg16_nt(wp[j][1] + bo);
+      if constexpr (W4) {
+        const int gi = kb / 32 + 2 * (lane & 3);
+        sl.st[j][0] = sp[j][min(gi, gmax)];
+        sl.st[j][1] = sp[j][min(gi + 1, gmax)];
+      }
+    }
+  };
+  const int wr = (wc >> 2) * 1024 + (wc & 3) * 256;
+  auto wstage = [&](const SkinnySlot<KIND, NB>& sl) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int R = 8 * h + (lane >> 3);
+        *reinterpret_cast<uint4*>(wslot + j * 2048 + wr + ((R ^ (2 * wc)) & 15) * 16) = sl.w[j][h];
+      }
+      if constexpr (W4)
+        *reinterpret_cast<uint32_t*>(sslot + j * 256 + (lane >> 2) * 16 + (lane & 3) * 4) =
+            (sl.st[j][0] & 0xFFFFu) | (sl.st[j][1] << 16);
+    }
+  };
+
+  // ---- activation chunks. Loads are clamped and stay unmasked in
+  // registers (masking them at load time would make the next instruction
+  // wait for every load in flight); the mask is applied by the LDS write.
+  uint4 aset[2][kPer];
+  auto aload = [&](int ci, uint4 (&dst)[kPer]) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int piece = (tid + 256 * q) % kRowPieces;
+      const int k = k0 + ci * 256 + piece * (16 / ESZ);
+      dst[q] = ldg16(ap[q] + (size_t)min(k, K - 16 / ESZ) * ESZ);
+    }
+  };
+  auto awrite = [&](const uint4 (&src)[kPer], int ci, int buf) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int pc = tid + 256 * q;
+      const int row = pc / kRowPieces, piece = pc % kRowPieces;
+      const int k = k0 + ci * 256 + piece * (16 / ESZ);
+      const uint32_t m = k < k1 ? am[q] : 0u;
+      const int mb = row >> 4, rr = row & 15;
+      const int s = piece / (8 * ESZ), c = piece % (8 * ESZ);
+      int off;
+      if constexpr (W4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
+      else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ (2 * c)) & 15) * 16;
+      const uint4 v = src[q];
+      *reinterpret_cast<uint4*>(lds + buf * kBuf + (mb * 2 + s) * kBlk + off) =
+          make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+    }
+  };
+  const int rd0 = g * 256 + ((r ^ (2 * g)) & 15) * 16;
+  const int rd1 = 1024 + g * 256 + ((r ^ (2 * (4 + g))) & 15) * 16;
+  const int rdw = g * 256;
+
+  // multiply the weight unit in the wave's slot (unit u) with the
+  // activation chunk that holds it
+  auto compute = [&](int u) {
+    const uint8_t* abase = lds + ((u / UPC) & 1) * kBuf;
+    if constexpr (W4) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        uint4 cw[NB];
+        float st[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          cw[j] = *reinterpret_cast<const uint4*>(wslot + j * 2048 + s * 1024 + g * 256 +
+                                                  ((r ^ (2 * (4 * s + g))) & 15) * 16);
+          st[j] = bf16_f32(*reinterpret_cast<const uint16_t*>(sslot + j * 256 + r * 16 + (4 * s + g) * 2));
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          v8bf bf[NB];
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const uint32_t word = w == 0 ? cw[j].x : w == 1 ? cw[j].y : w == 2 ? cw[j].z : cw[j].w;
+            bf[j] = dequant8(word, st[j], -8.0f * st[j]);
+          }
+          const int off = s * kBlk + w * 1024 + rdw + ((r ^ (4 * g + w)) & 15) * 16;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const v8bf af = *reinterpret_cast<const v8bf*>(abase + mb * 2 * kBlk + off);
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[mb][j] = mfma_bf16(af, bf[j], acc[mb][j]);
+          }
+        }
+      }
+    } else {
+      const uint8_t* ab = abase + (u & 1) * kBlk;
+      v4i w0[NB], w1[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        w0[j] = *reinterpret_cast<const v4i*>(wslot + j * 2048 + rd0);
+        w1[j] = *reinterpret_cast<const v4i*>(wslot + j * 2048 + rd1);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const v4i a0 = *reinterpret_cast<const v4i*>(ab + mb * 2 * kBlk + rd0);
+        const v4i a1 = *reinterpret_cast<const v4i*>(ab + mb * 2 * kBlk + rd1);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if constexpr (KIND == kGemmFP8) {
+            acc[mb][j] = mfma_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                  __builtin_shufflevector(w0[j], w1[j], 0, 1, 2, 3, 4, 5, 6, 7), acc[mb][j]);
+          } else {
+            acc[mb][j] = mfma_i8(a0, w0[j], acc[mb][j]);
+            acc[mb][j] = mfma_i8(a1, w1[j], acc[mb][j]);
+          }
+        }
+      }
+    }
+  };
+
+  // ---- prologue: activation chunks 0 and 1 in registers, chunk 0 in LDS,
+  // the weight ring filled
+  aload(0, aset[0]);
+  aload(1, aset[1]);
+  SkinnySlot<KIND, NB> ring[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) wload(ring[d], d);
+  awrite(aset[0], 0, 0);
+  __syncthreads();
+
+  // ---- main loop over whole rounds of DEPTH units. Activation chunk ci
+  // uses LDS buffer ci & 1 and register set ci & 1; at its start the set is
+  // refilled with chunk ci + 2, after its last unit chunk ci + 1 goes to the
+  // other buffer. Each unit: its registers go to the wave's slot, the ring
+  // slot is refilled DEPTH units ahead (past the range: clamped loads of
+  // valid memory, never used), then the unit is multiplied. The scheduling
+  // barriers keep each refill right after the write that freed its slot.
+  const int full = nunits / DEPTH, rem = nunits % DEPTH;
+  for (int rd = 0; rd < full; ++rd) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int u = rd * DEPTH + d;
+      if (d % UPC == 0) aload(u / UPC + 2, aset[(d / UPC) & 1]);
+      wstage(ring[d]);
+      __builtin_amdgcn_sched_barrier(0);
+      wload(ring[d], u + DEPTH);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u);
+      if (d % UPC == UPC - 1) {
+        awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+  // ---- the last rem units are already in the ring; the activation chunks
+  // continue as above. The condition is uniform over the workgroup.
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) {
+    if (d < rem) {
+      const int u = full * DEPTH + d;
+      if (d % UPC == 0) aload(u / UPC + 2, aset[(d / UPC) & 1]);
+      wstage(ring[d]);
+      compute(u);
+      if (d % UPC == UPC - 1 && d + 1 < rem) {
+        awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+}
+
+}  // namespace qlin
