@@ -59,14 +59,26 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  // exclusive prefix over the experts by the first wave, 64 at a time
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     int run = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = run;
-      cur[e] = run;
-      run += cnt[e];
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < E ? cnt[e] : 0;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      if (e < E) {
+        off[e] = run + incl - c;
+        cur[e] = run + incl - c;
+      }
+      run += __shfl(incl, 63, 64);
     }
-    off[E] = run;
+    if (lane == 0) off[E] = run;
   }
   __syncthreads();
   for (int r = threadIdx.x; r < R; r += blockDim.x) {
@@ -94,15 +106,23 @@ struct MoeGemmArgs {
 // the expert's routed rows at a time; the weights stream once per row block
 // through the skinny GEMM core (qlin_skinny.h), gathered activation rows
 // pass through LDS.
+// gate_up: each wave owns 16 gate columns and the matching 16 up columns
+// (NB = 2 blocks); down: each wave owns two blocks of 16 columns, 128
+// columns per workgroup, so that its short K (I) still streams enough bytes
+// per workgroup.
+template <bool GATEUP>
+constexpr int moe_cols_per_wg() { return GATEUP ? 64 : 128; }
+
 template <bool GATEUP, int MB>
 __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int e, int rbeg, int nrows) {
-  constexpr int NB = GATEUP ? 2 : 1;
-  constexpr int DEPTH = (GATEUP || MB > 2) ? 4 : 8;
+  constexpr int NB = 2;
+  constexpr int DEPTH = 4;
+  constexpr int CW = GATEUP ? 16 : 32;  // distinct output columns per wave
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K;
-  const int c0 = blockIdx.x * 64 + wave * 16;  // this wave's first output column
+  const int c0 = blockIdx.x * moe_cols_per_wg<GATEUP>() + wave * CW;  // this wave's first output column
   const size_t wrows = GATEUP ? 2 * (size_t)p.nout : (size_t)p.nout;
   const uint8_t* wbase = p.W + (size_t)e * wrows * K;
 
@@ -112,8 +132,9 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
   for (int j = 0; j < NB; ++j) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int col = min(c0 + 8 * h + (lane >> 3), p.nout - 1);
-      wp[j][h] = wbase + (size_t)(j * p.nout + col) * K + 16 * (lane & 7);
+      // gate_up block j: bank rows j*I + column; down block j: column 16j + ..
+      const int col = min(c0 + (GATEUP ? 0 : 16 * j) + 8 * h + (lane >> 3), p.nout - 1);
+      wp[j][h] = wbase + (size_t)((GATEUP ? j * p.nout : 0) + col) * K + 16 * (lane & 7);
     }
     sp[j] = nullptr;
   }
@@ -126,8 +147,15 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
     ap[q] = p.A + (size_t)(GATEUP ? rr / p.topk : rr) * K;
     am[q] = i < nrows ? 0xFFFFFFFFu : 0u;
   }
-  // epilogue operands (output rows 4g+q of each block, this lane's column)
-  const int col = c0 + r, colc = min(col, p.nout - 1);
+  v4f acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+  skinny_mma<kGemmFP8, MB, NB, DEPTH>(lds, wp, sp, ap, am, K, 0, K, acc);
+
+  // epilogue operands (output rows 4g+q of each block, this lane's column),
+  // fetched after the main loop so that they hold no registers during it
   int rid[MB][4];
   float sav[MB][4];
 #pragma unroll
@@ -138,59 +166,56 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
       rid[i][q] = rr;
       sav[i][q] = p.sa[GATEUP ? rr / p.topk : rr];
     }
-  float swv[NB];
-  swv[0] = p.sw[(size_t)e * wrows + colc];
-  if (GATEUP) swv[NB - 1] = p.sw[(size_t)e * wrows + p.nout + colc];
-
-  v4f acc[MB][NB];
+  if constexpr (GATEUP) {
+    const int col = c0 + r, colc = min(col, p.nout - 1);
+    const float swg = p.sw[(size_t)e * wrows + colc];
+    const float swu = p.sw[(size_t)e * wrows + p.nout + colc];
+    if (col < p.nout) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
-  skinny_mma<kGemmFP8, MB, NB, DEPTH>(lds, wp, sp, ap, am, K, 0, K, acc);
-
-  if (col < p.nout) {
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = i * 16 + 4 * g + q;
-        if (row < nrows) {
-          const int rr = rid[i][q];
-          if (GATEUP) {
-            const float gv = (acc[i][0][q] * sav[i][q]) * swv[0];
-            const float uv = (acc[i][1][q] * sav[i][q]) * swv[NB - 1];
+        for (int q = 0; q < 4; ++q) {
+          if (i * 16 + 4 * g + q < nrows) {
+            const float gv = (acc[i][0][q] * sav[i][q]) * swg;
+            const float uv = (acc[i][1][q] * sav[i][q]) * swu;
             const float silu = gv / (1.0f + expf(-gv));
-            p.out[(size_t)rr * p.nout + col] = silu * uv;
-          } else {
-            p.out[(size_t)rr * p.nout + col] = (acc[i][0][q] * sav[i][q]) * swv[0];
+            p.out[(size_t)rid[i][q] * p.nout + col] = silu * uv;
           }
         }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int col = c0 + 16 * j + r;
+      const float sw = p.sw[(size_t)e * wrows + min(col, p.nout - 1)];
+      if (col < p.nout) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (i * 16 + 4 * g + q < nrows) p.out[(size_t)rid[i][q] * p.nout + col] = (acc[i][j][q] * sav[i][q]) * sw;
       }
+    }
   }
   __syncthreads();  // the next row block reuses the LDS
 }
 
-// Row blocks of up to 64 rows; the LARGE instantiation serves blocks of 33..64
-// rows, the other one blocks of 1..32 rows, so that the common small blocks
-// do not pay the registers (and occupancy) of the large ones. Workgroups
-// with nothing to do return at once.
-template <bool GATEUP, bool LARGE>
+// Each workgroup walks its expert's routed rows in blocks of MBMAX*16 rows
+// (one pass of the weights per block). MBMAX is chosen per call from the
+// average number of rows per expert: 2 (32-row blocks) for light loads, 3
+// (48-row blocks) otherwise, so that nearly every expert is served by one
+// pass while the registers still allow two workgroups per CU.
+template <bool GATEUP, int MBMAX>
 __global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeGemmArgs p) {
-  constexpr int NB = GATEUP ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<kGemmFP8, LARGE ? 4 : 2, NB>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<kGemmFP8, MBMAX, 2>()];
   const int e = blockIdx.y;
   const int beg = p.off[e], n = p.off[e + 1] - beg;
-  for (int rb = 0; rb < n; rb += 64) {
-    const int nr = min(64, n - rb);
+  for (int rb = 0; rb < n; rb += 16 * MBMAX) {
+    const int nr = min(16 * MBMAX, n - rb);
     const int mb = (nr + 15) / 16;
-    if constexpr (LARGE) {
-      if (mb == 3) moe_tile<GATEUP, 3>(p, lds, e, beg + rb, nr);
-      else if (mb == 4) moe_tile<GATEUP, 4>(p, lds, e, beg + rb, nr);
-    } else {
-      if (mb == 1) moe_tile<GATEUP, 1>(p, lds, e, beg + rb, nr);
-      else if (mb == 2) moe_tile<GATEUP, 2>(p, lds, e, beg + rb, nr);
-    }
+    if (mb == 1) moe_tile<GATEUP, 1>(p, lds, e, beg + rb, nr);
+    else if (mb == 2 || MBMAX == 2) moe_tile<GATEUP, 2>(p, lds, e, beg + rb, nr);
+    else moe_tile<GATEUP, (MBMAX > 2 ? 3 : 2)>(p, lds, e, beg + rb, nr);
   }
 }
 
@@ -242,21 +267,21 @@ int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E
   moe_route_kernel<<<1, 1024, 2 * E * sizeof(int), st>>>(ids, R, (int)E, off, rows);
   if ((rc = launch_status())) return rc;
 
-  // every expert's rows fit one small block when T*topk/E is small; the
-  // large-block launches are skipped when no expert can reach 33 rows
-  const bool any_large = R > 32;
+  // row blocks of 32 rows when an expert averages at most 8 routed rows,
+  // else 48
+  const bool light = R <= 8 * E;
   MoeGemmArgs gu{xq, sx, w13, s13, off, rows, topk, (int)H, (int)I, act};
-  const dim3 ggrid((unsigned)((I + 63) / 64), (unsigned)E);
-  moe_gemm_kernel<true, false><<<ggrid, 256, 0, st>>>(gu);
-  if (any_large) moe_gemm_kernel<true, true><<<ggrid, 256, 0, st>>>(gu);
+  const dim3 ggrid((unsigned)((I + moe_cols_per_wg<true>() - 1) / moe_cols_per_wg<true>()), (unsigned)E);
+  if (light) moe_gemm_kernel<true, 2><<<ggrid, 256, 0, st>>>(gu);
+  else moe_gemm_kernel<true, 3><<<ggrid, 256, 0, st>>>(gu);
   if ((rc = launch_status())) return rc;
 
   if ((rc = launch_quant_rows_f32(act, R, I, aq, sa, st))) return rc;
 
   MoeGemmArgs dn{aq, sa, w2, s2, off, rows, topk, (int)I, (int)H, dd};
-  const dim3 dgrid((unsigned)((H + 63) / 64), (unsigned)E);
-  moe_gemm_kernel<false, false><<<dgrid, 256, 0, st>>>(dn);
-  if (any_large) moe_gemm_kernel<false, true><<<dgrid, 256, 0, st>>>(dn);
+  const dim3 dgrid((unsigned)((H + moe_cols_per_wg<false>() - 1) / moe_cols_per_wg<false>()), (unsigned)E);
+  if (light) moe_gemm_kernel<false, 2><<<dgrid, 256, 0, st>>>(dn);
+  else moe_gemm_kernel<false, 3><<<dgrid, 256, 0, st>>>(dn);
   if ((rc = launch_status())) return rc;
 
   const long long threads = T * (H / 4);
