@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--kernel-iters", type=int, default=64,
                     help="event-timed launches per kernel for the per-kernel rows")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="counter-collection workload: every decode GEMM of the step, 8 eager "
+                         "launches each, then a 256 MiB device copy (the counters' calibration); "
+                         "run under rocprofv3 --pmc")
     return ap.parse_args()
 
 
@@ -101,6 +105,44 @@ class Timer:
             ev[i][1].record(st)
         torch.cuda.synchronize()
         d = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)  # us
+        return dict(mean_us=sum(d) / len(d), median_us=d[len(d) // 2], min_us=d[0])
+
+
+class GraphTimer:
+    """Average device time per launch: `reps` launches of one call (rotating
+    over weight copies) captured in one HIP graph, replayed with events
+    around each replay on the replaying stream; time per launch = replay
+    time / reps. Back-to-back graph launches leave little idle time between
+    kernels, so this agrees with the profiler's kernel durations."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, reps=32, replays=5):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(2):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        g.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(replays)]
+        for a, b in ev:
+            a.record(st)
+            g.replay()
+            b.record(st)
+        torch.cuda.synchronize()
+        d = sorted(a.elapsed_time(b) * 1e3 / reps for a, b in ev)  # us per launch
+        del g
         return dict(mean_us=sum(d) / len(d), median_us=d[len(d) // 2], min_us=d[0])
 
 
@@ -177,43 +219,63 @@ def make_bufs(torch, Ms, N, K):
     return out
 
 
-def per_kernel_rows(q, torch, L, x, Ms, bufs, iters, tag):
-    """Event-timed GEMM launches (quantised activations prepared outside)."""
-    T = Timer(torch)
-    rows = {}
+def gemm_calls(q, L, x, Ms, bufs):
+    """(row name suffix, M, format, call(i)) for every decode GEMM of the step
+    and the FP8 activation quantisation (operands prepared outside)."""
+    out = []
     for M in Ms:
         b = bufs[M]
         xm = x[:M]
         q.quant_act(xm, "e4m3", out=(b["aq8"], b["sa8"]))
         q.quant_act(xm, "int8", out=(b["aqi"], b["sai"]))
-        calls = {
-            "fp8": lambda i, b=b: q.gemm_fp8(b["aq8"], b["sa8"], *L.fp8[i % L.copies], out=b["y8"]),
-            "int8": lambda i, b=b: q.gemm_w8a8(b["aqi"], b["sai"], *L.int8[i % L.copies], out=b["yi"]),
-            "w4a16": lambda i, xm=xm, b=b: q.gemm_w4a16(xm, *L.w4[i % L.copies], out=b["y4"]),
-            "quant_fp8": lambda i, xm=xm, b=b: q.quant_act(xm, "e4m3", out=(b["aq8"], b["sa8"])),
-        }
-        for fmt, fn in calls.items():
-            t = T.time(fn, iters)
-            r = dict(M=M, us=round(t["mean_us"], 3), median_us=round(t["median_us"], 3))
-            if fmt != "quant_fp8":
-                wb = weight_bytes(fmt, L.N, L.K)
-                r["weight_bytes"] = wb
-                r["GBps"] = round(wb / (t["mean_us"] * 1e3), 1)
-                r["frac_hbm"] = round(r["GBps"] / HBM_PEAK_GBS, 4)
-            rows[f"{tag}_{fmt}_M{M}"] = r
+        out += [
+            (f"fp8_M{M}", M, "fp8",
+             lambda i, b=b: q.gemm_fp8(b["aq8"], b["sa8"], *L.fp8[i % L.copies], out=b["y8"])),
+            (f"int8_M{M}", M, "int8",
+             lambda i, b=b: q.gemm_w8a8(b["aqi"], b["sai"], *L.int8[i % L.copies], out=b["yi"])),
+            (f"w4a16_M{M}", M, "w4a16",
+             lambda i, xm=xm, b=b: q.gemm_w4a16(xm, *L.w4[i % L.copies], out=b["y4"])),
+            (f"quant_fp8_M{M}", M, "quant_fp8",
+             lambda i, xm=xm, b=b: q.quant_act(xm, "e4m3", out=(b["aq8"], b["sa8"]))),
+        ]
+    return out
+
+
+def per_kernel_rows(q, torch, L, x, Ms, bufs, iters, tag):
+    """Per-launch device time of each GEMM of the step (graph-timed, see
+    GraphTimer), weight GB/s and the fraction of the HBM peak."""
+    T = GraphTimer(torch)
+    rows = {}
+    for name, M, fmt, fn in gemm_calls(q, L, x, Ms, bufs):
+        t = T.time(fn, reps=min(32, max(8, iters // 2)))
+        r = dict(M=M, us=round(t["mean_us"], 3), min_us=round(t["min_us"], 3))
+        if fmt != "quant_fp8":
+            wb = weight_bytes(fmt, L.N, L.K)
+            r["weight_bytes"] = wb
+            r["GBps"] = round(wb / (t["mean_us"] * 1e3), 1)
+            r["frac_hbm"] = round(r["GBps"] / HBM_PEAK_GBS, 4)
+        rows[f"{tag}_{name}"] = r
     return rows
 
 
 def bf16_rows(torch, L, x, Ms, iters, tag):
-    T = Timer(torch)
+    """torch's bf16 GEMM on the materialised weights (the comparator): the
+    faster of x @ W^T and (W @ x^T)^T, graph-timed like the other rows."""
+    T = GraphTimer(torch)
     ws = [L.w_bf16.clone() for _ in range(max(4, int(math.ceil(1.5 * GIB / (2 * L.N * L.K)))))]
     rows = {}
     for M in Ms:
-        xm = x[:M]
-        t = T.time(lambda i, xm=xm: torch.matmul(xm, ws[i % len(ws)].t()), iters)
+        xm = x[:M].contiguous()
+        xt = xm.t().contiguous()
+        best = None
+        for form, fn in (("x@Wt", lambda i, xm=xm: torch.matmul(xm, ws[i % len(ws)].t())),
+                         ("(W@xt)t", lambda i, xt=xt: torch.matmul(ws[i % len(ws)], xt))):
+            t = T.time(fn, reps=min(16, len(ws)))
+            if best is None or t["mean_us"] < best[1]["mean_us"]:
+                best = (form, t)
         wb = weight_bytes("bf16", L.N, L.K)
-        rows[f"{tag}_bf16_torch_M{M}"] = dict(M=M, us=round(t["mean_us"], 3),
-                                             GBps=round(wb / (t["mean_us"] * 1e3), 1))
+        rows[f"{tag}_bf16_torch_M{M}"] = dict(M=M, us=round(best[1]["mean_us"], 3), form=best[0],
+                                             GBps=round(wb / (best[1]["mean_us"] * 1e3), 1))
     del ws
     return rows
 
@@ -319,6 +381,65 @@ def c5_rows(q, torch, gen, iters):
 
 
 # ----------------------------------------------------------------------------
+# HBM traffic from hardware counters
+# ----------------------------------------------------------------------------
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "decode_gemm_K2048_N8192_pmc_traffic.md")
+DECODE_SOURCES = ("qlin_gemm_decode.hip", "qlin_skinny.h", "qlin_device.h")
+
+
+def decode_sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "quantized_linear_layers_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def pmc_pass(q, torch, L, x, Ms, bufs, launches=8):
+    """Counter-collection workload (run under rocprofv3 --pmc): every decode
+    GEMM of the step, `launches` eager launches each in a fixed order, then a
+    plain 256 MiB device-to-device copy four times, whose FETCH_SIZE /
+    WRITE_SIZE readings calibrate the counters (known bytes / reading)."""
+    order = []
+    for name, M, fmt, fn in gemm_calls(q, L, x, Ms, bufs):
+        if fmt == "quant_fp8":
+            continue
+        torch.cuda.synchronize()
+        for i in range(launches):
+            fn(i)
+        torch.cuda.synchronize()
+        order.append("C2_" + name)
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_pass": order, "launches": launches, "copy_bytes": n, "copies": 4,
+                      "sources_sha256": decode_sources_sha256()}), flush=True)
+
+
+def traffic_table():
+    """Per-launch HBM bytes of each decode GEMM of the step, from the
+    committed counter summary, if it was taken on the current kernel sources
+    (else None: the counters no longer describe this code)."""
+    try:
+        with open(TRAFFIC_MD) as fh:
+            txt = fh.read()
+        blob = txt[txt.index("```json") + 7:]
+        blob = blob[:blob.index("```")]
+        tab = json.loads(blob)
+    except (OSError, ValueError):
+        return None
+    if tab.get("sources_sha256") != decode_sources_sha256():
+        return None
+    return tab
+
+
+# ----------------------------------------------------------------------------
 # CPU baseline: the oracle running the same step on the host
 # ----------------------------------------------------------------------------
 def cpu_baseline(gen, d, Ms, step_weight_bytes, budget_s=12.0):
@@ -379,6 +500,9 @@ def main():
     L = DecodeLayer(q, torch, d, copies)
     x = dev(d["a"], torch)
     bufs = make_bufs(torch, Ms, N, K)
+    if a.pmc_pass:
+        pmc_pass(q, torch, L, x, Ms, bufs)
+        return
     step = run_step_fn(q, torch, L, x, Ms, bufs)
 
     # capture one graph per rotation slot (eager warm-up first)
@@ -422,10 +546,17 @@ def main():
     fmt_dom = dom.split("_")[1]
     kname = {"fp8": "decode_gemm_kernel<FP8>", "int8": "decode_gemm_kernel<INT8>",
              "w4a16": "decode_gemm_kernel<W4A16>"}[fmt_dom]
+    tab = traffic_table()
+    traffic = None
+    if tab and dom in tab.get("rows", {}):
+        traffic = tab["rows"][dom]["hbm_bytes"]
     roofline = dict(bound="hbm", achieved=dr["GBps"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(dr["GBps"] / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(dr["GBps"] / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel=f"{kname} M={dr['M']}", bytes_per_launch=dr["weight_bytes"],
-                    launch_us=dr["us"])
+                    launch_us=dr["us"],
+                    traffic_note="HBM bytes per launch from FETCH_SIZE + WRITE_SIZE (rocprofv3 "
+                                 "--pmc), calibrated on a 256 MiB copy; null when the counters "
+                                 "were taken on other kernel sources")
     del graphs
     del L
     torch.cuda.empty_cache()
