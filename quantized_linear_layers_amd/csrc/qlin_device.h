@@ -99,6 +99,45 @@ __device__ __forceinline__ v8bf dequant8(uint32_t word, float step, float neg8st
   return __builtin_bit_cast(v8bf, q);
 }
 
+// The same dequantisation with the 8 values in the order k = 0, 2, 4, 6, 1,
+// 3, 5, 7: even nibbles are the low nibble of each byte, so one AND exposes
+// four of them as bytes (converted by v_cvt_f32_ubyte{0..3}), one shift and
+// AND the odd ones. The activation operand must use the same order
+// (perm_even_odd_bf16).
+template <int B>
+__device__ __forceinline__ float cvt_f32_ubyte(uint32_t x) {
+  float f;
+  if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
+  else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
+  else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
+  return f;
+}
+
+__device__ __forceinline__ v8bf dequant8_eo(uint32_t word, float step, float neg8step) {
+  const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+  float f[8];
+  f[0] = __builtin_fmaf(cvt_f32_ubyte<0>(lo), step, neg8step);
+  f[1] = __builtin_fmaf(cvt_f32_ubyte<1>(lo), step, neg8step);
+  f[2] = __builtin_fmaf(cvt_f32_ubyte<2>(lo), step, neg8step);
+  f[3] = __builtin_fmaf(cvt_f32_ubyte<3>(lo), step, neg8step);
+  f[4] = __builtin_fmaf(cvt_f32_ubyte<0>(hi), step, neg8step);
+  f[5] = __builtin_fmaf(cvt_f32_ubyte<1>(hi), step, neg8step);
+  f[6] = __builtin_fmaf(cvt_f32_ubyte<2>(hi), step, neg8step);
+  f[7] = __builtin_fmaf(cvt_f32_ubyte<3>(hi), step, neg8step);
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  v4i q = {(int)p[0], (int)p[1], (int)p[2], (int)p[3]};
+  return __builtin_bit_cast(v8bf, q);
+}
+
+// 8 bf16 values k = 0..7 (16 bytes) reordered to k = 0, 2, 4, 6, 1, 3, 5, 7.
+__device__ __forceinline__ uint4 perm_even_odd_bf16(uint4 v) {
+  return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                    __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -24,7 +24,9 @@
 //      bf16 activations (4 KB per block and step): piece = MFMA w of the
 //        step, chunk c = 4g + w (values k = 32g + 8w .. +8), f = c.
 //  * the int4 unpack (bf16(c * step), exact product, one rounding) happens
-//    right before the MFMAs.
+//    right before the MFMAs, in the K order 0,2,4,6,1,3,5,7 within each 8
+//    (cheaper nibble extraction); the activations are stored in LDS in the
+//    same order, which leaves every dot product unchanged.
 // Output layout (MFMA): acc[mb][j] register i of lane (r, g) is row
 // mb*16 + 4g + i, column 16j + r of the wave's columns.
 #pragma once
@@ -146,7 +148,8 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
       int off;
       if constexpr (W4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
       else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ (2 * c)) & 15) * 16;
-      const uint4 v = src[q];
+      uint4 v = src[q];
+      if constexpr (W4) v = perm_even_odd_bf16(v);  // the order of dequant8_eo
       *reinterpret_cast<uint4*>(lds + buf * kBuf + (mb * 2 + s) * kBlk + off) =
           make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
     }
@@ -176,7 +179,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
             const uint32_t word = w == 0 ? cw[j].x : w == 1 ? cw[j].y : w == 2 ? cw[j].z : cw[j].w;
-            bf[j] = dequant8(word, st[j], -8.0f * st[j]);
+            bf[j] = dequant8_eo(word, st[j], -8.0f * st[j]);
           }
           const int off = s * kBlk + w * 1024 + rdw + ((r ^ (4 * g + w)) & 15) * 16;
 #pragma unroll
