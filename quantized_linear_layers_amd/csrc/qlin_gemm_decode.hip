@@ -55,13 +55,13 @@ struct GemmArgs {
 // Decode-shaped GEMM: the streaming core of qlin_skinny.h over this
 // workgroup's 64*NB columns and this split's K range, then the split-K
 // reduction and the epilogue.
-template <int KIND, int MB, int NB, int DEPTH>
+template <int KIND, int MB, int NB, int DEPTH, bool SB>
 __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   using Acc = SkinnyAcc<KIND>;
   constexpr bool W4 = KIND == kGemmW4;
   constexpr int ESZ = W4 ? 2 : 1;
   constexpr int kPer = MB * ESZ;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<KIND, MB, NB>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<KIND, MB, NB, DEPTH>()];
   __shared__ unsigned last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
       const int row = min(n0 + 16 * j + 8 * h + (lane >> 3), p.N - 1);
       wp[j][h] = p.W + (size_t)row * (W4 ? p.K / 2 : p.K) + 16 * (lane & 7);
     }
-    sp[j] = W4 ? p.steps + (size_t)min(n0 + 16 * j + (lane >> 2), p.N - 1) * (p.K / 32) : nullptr;
+    sp[j] = W4 ? p.steps + (size_t)min(n0 + 16 * j + (lane & 15), p.N - 1) * (p.K / 32) : nullptr;
   }
   const uint8_t* ap[kPer];
   uint32_t am[kPer];
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
-  skinny_mma<KIND, MB, NB, DEPTH>(lds, wp, sp, ap, am, p.K, k0, k1, acc);
+  skinny_mma<KIND, MB, NB, DEPTH, SB>(lds, wp, sp, ap, am, p.K, k0, k1, acc);
 
   // ---- split-K: publish partials, the last workgroup of the tile reduces
   float accf[MB][NB][4];
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
 // launch configuration
 // ----------------------------------------------------------------------------
 struct DecodeCfg {
-  int MB, NB, DEPTH;
+  int MB, NB;
   int tiles, S, kc;
 };
 
@@ -235,8 +235,7 @@ static int decode_nb(int kind, int MB) {
 // Grid: 64*NB columns per workgroup, S splits of K. Split-K costs a write
 // and a read of S*M*N partial sums, so it is used only to reach about three
 // quarters of the CUs with column tiles; each split keeps >= 4 steps of
-// 128 K. DEPTH (weight units in flight per wave) is as large as the
-// registers allow.
+// 128 K.
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   c.MB = (int)((M + 15) / 16);
@@ -253,26 +252,32 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   steps_per = (steps_per + 1) / 2 * 2;  // whole 256-K chunks
   c.kc = (int)(steps_per * 128);
   c.S = (int)((K + c.kc - 1) / c.kc);
-  c.DEPTH = c.MB <= 2 ? (kind == kGemmW4 ? 4 : 8) : (kind == kGemmW4 ? 2 : 4);
   return c;
 }
 
-// Dispatch on (kind, MB, DEPTH) to the instantiation that serves it.
+// Dispatch on (kind, MB, bulk steps) to the instantiation that serves it.
+// DEPTH (weight units in flight per wave) per (kind, MB), as measured: 8
+// fp8/int8 128-K units at MB <= 2, 4 above; int4 256-K units: 2 at MB = 1
+// (deeper rings were slower), 4 at MB = 2, 2 above (register bound).
 template <typename F>
-static auto with_decode_inst(int kind, int MB, int DEPTH, F&& f) {
-#define QLIN_DEC(K, NB1, NB2, D)                                                        \
-  switch (MB) {                                                                          \
-    case 1: return f.template operator()<K, 1, NB1, 2 * D>();                            \
-    case 2: return f.template operator()<K, 2, NB2, 2 * D>();                            \
-    case 3: return f.template operator()<K, 3, 2, D>();                                  \
-    default: return f.template operator()<K, 4, 2, D>();                                 \
+static auto with_decode_inst(int kind, int MB, bool sb, F&& f) {
+#define QLIN_DEC(K, NB1, NB2, D1, D2, D3, SB)                 \
+  switch (MB) {                                              \
+    case 1: return f.template operator()<K, 1, NB1, D1, SB>(); \
+    case 2: return f.template operator()<K, 2, NB2, D2, SB>(); \
+    case 3: return f.template operator()<K, 3, 2, D3, SB>();   \
+    default: return f.template operator()<K, 4, 2, D3, SB>();  \
   }
   if (kind == kGemmW4) {
-    QLIN_DEC(kGemmW4, 1, 2, 2)
+    if (sb) {
+      QLIN_DEC(kGemmW4, 1, 2, 2, 4, 2, true)
+    } else {
+      QLIN_DEC(kGemmW4, 1, 2, 2, 4, 2, false)
+    }
   } else if (kind == kGemmI8) {
-    QLIN_DEC(kGemmI8, 1, 1, 4)
+    QLIN_DEC(kGemmI8, 1, 1, 8, 8, 4, false)
   } else {
-    QLIN_DEC(kGemmFP8, 1, 1, 4)
+    QLIN_DEC(kGemmFP8, 1, 1, 8, 8, 4, false)
   }
 #undef QLIN_DEC
 }
@@ -293,9 +298,9 @@ struct LaunchFn {
   const GemmArgs* a;
   const DecodeCfg* c;
   hipStream_t st;
-  template <int KIND, int MB, int NB, int DEPTH>
+  template <int KIND, int MB, int NB, int DEPTH, bool SB>
   int operator()() const {
-    decode_gemm_kernel<KIND, MB, NB, DEPTH><<<dim3((unsigned)c->tiles, (unsigned)c->S), 256, 0, st>>>(*a);
+    decode_gemm_kernel<KIND, MB, NB, DEPTH, SB><<<dim3((unsigned)c->tiles, (unsigned)c->S), 256, 0, st>>>(*a);
     return 0;
   }
 };
@@ -322,7 +327,9 @@ int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const v
     g.cnt = reinterpret_cast<unsigned*>(ws);
     g.part = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ws) + kCounterBytes);
   }
-  with_decode_inst(kind, c.MB, c.DEPTH, LaunchFn{&g, &c, st});
+  // int4 steps in 16-byte pieces of 8 groups: aligned rows, whole pieces
+  const bool sb = kind == kGemmW4 && K % 256 == 0 && ((uintptr_t)wsc & 15) == 0;
+  with_decode_inst(kind, c.MB, sb, LaunchFn{&g, &c, st});
   return launch_status();
 }
 

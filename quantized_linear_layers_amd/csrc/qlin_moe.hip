@@ -207,7 +207,7 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
 // pass while the registers still allow two workgroups per CU.
 template <bool GATEUP, int MBMAX>
 __global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeGemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<kGemmFP8, MBMAX, 2>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<kGemmFP8, MBMAX, 2, 1>()];
   const int e = blockIdx.y;
   const int beg = p.off[e], n = p.off[e + 1] - beg;
   for (int rb = 0; rb < n; rb += 16 * MBMAX) {

@@ -5,8 +5,9 @@
 // one K range [k0, k1):
 //  * activations pass through LDS in chunks of 256 K, double buffered and
 //    shared by the 4 waves (one barrier per chunk), fetched once per
-//    workgroup in whole cache lines; rows past the valid count and K past
-//    the range are zeroed when written;
+//    workgroup in whole cache lines; K past the range is zeroed when
+//    written; rows past the valid count are zeroed once, and waves whose
+//    share of a chunk holds no valid row skip its loads and writes;
 //  * each wave streams its own 16*NB weight rows in "units" (16 rows x 128
 //    bytes per 16-row block: 128 K of fp8/int8, 256 K of int4 codes) with
 //    line-shaped nontemporal loads (8 rows x 128 B per instruction), DEPTH
@@ -23,10 +24,13 @@
 //        chunk c = 4s + g (the 32 codes of group 4s + g), f = 2c;
 //      bf16 activations (4 KB per block and step): piece = MFMA w of the
 //        step, chunk c = 4g + w (values k = 32g + 8w .. +8), f = c.
-//  * the int4 unpack (bf16(c * step), exact product, one rounding) happens
-//    right before the MFMAs, in the K order 0,2,4,6,1,3,5,7 within each 8
-//    (cheaper nibble extraction); the activations are stored in LDS in the
-//    same order, which leaves every dot product unchanged.
+//  * int4 group steps: with SB (16-byte aligned step rows, K % 256 == 0)
+//    one 16-byte load per lane fetches the steps of 16 rows x DEPTH units
+//    once per round of DEPTH units, into a wave-private LDS slot of DEPTH
+//    units; otherwise each unit loads its own (4-byte granules of 2-byte
+//    loads). Step slot layout: (unit * NB + j) * 256 + row * 16 + group * 2;
+//  * the int4 unpack (bf16(c * step), exact product, one rounding, by
+//    dequant8_mix) happens right before the MFMAs.
 // Output layout (MFMA): acc[mb][j] register i of lane (r, g) is row
 // mb*16 + 4g + i, column 16j + r of the wave's columns.
 #pragma once
@@ -41,10 +45,10 @@ namespace qlin {
 template <int KIND>
 using SkinnyAcc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
 
-// Per-workgroup LDS bytes of skinny_mma<KIND, MB, NB>.
-template <int KIND, int MB, int NB>
+// Per-workgroup LDS bytes of skinny_mma<KIND, MB, NB, DEPTH>.
+template <int KIND, int MB, int NB, int DEPTH>
 constexpr int skinny_lds_bytes() {
-  return 2 * MB * 2 * 16 * 128 * (KIND == kGemmW4 ? 2 : 1) + 4 * NB * (2048 + (KIND == kGemmW4 ? 256 : 0));
+  return 2 * MB * 2 * 16 * 128 * (KIND == kGemmW4 ? 2 : 1) + 4 * NB * (2048 + (KIND == kGemmW4 ? 256 * DEPTH : 0));
 }
 
 // One weight unit of one wave in registers.
@@ -61,13 +65,14 @@ struct SkinnySlot<kGemmW4, NB> {
 // Inputs of one tile, per lane:
 //  wp[j][h]  weight row of block j, tile row 8h + lane/8, already offset by
 //            16 * (lane % 8) bytes (clamped onto a valid row);
-//  sp[j]     int4 group steps of tile row lane/4 of block j (W4A16 only);
+//  sp[j]     int4 group steps of tile row lane%16 of block j (W4A16 only);
 //  wbytes    weight bytes per row (K or K/2);
 //  ap[q]     activation row of this thread's chunk piece q (row
 //            (tid + 256q) / (16 * ESZ) of the tile; clamped onto a valid row)
-//  am[q]     0xFFFFFFFF if that row is a real row, else 0;
+//  am[q]     0xFFFFFFFF if that row is a real row, else 0 (the real rows
+//            must be a prefix of the tile's rows);
 //  K         full K (clamps the activation loads), k0/k1 the range.
-template <int KIND, int MB, int NB, int DEPTH>
+template <int KIND, int MB, int NB, int DEPTH, bool SB = false>
 __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB][2], const uint16_t* (&sp)[NB],
                                            const uint8_t* (&ap)[MB * (KIND == kGemmW4 ? 2 : 1)],
                                            uint32_t (&am)[MB * (KIND == kGemmW4 ? 2 : 1)], int K, int k0,
@@ -82,7 +87,8 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   constexpr int kRowPieces = 16 * ESZ;               // 16-byte pieces per row per chunk
   constexpr int kPer = MB * ESZ;                     // activation pieces per thread per chunk
   constexpr int kWSlot = NB * 2048;                  // one wave's weight unit in LDS
-  constexpr int kSSlot = W4 ? NB * 256 : 0;          // ... and its int4 group steps
+  constexpr int kSSlot = W4 ? DEPTH * NB * 256 : 0;  // ... and its int4 group steps
+  static_assert(!SB || (W4 && DEPTH <= 4), "bulk steps: W4A16, one load covers <= 4 units");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -102,8 +108,8 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
     for (int j = 0; j < NB; ++j) {
       sl.w[j][0] = ldg16_nt(wp[j][0] + bo);
       sl.w[j][1] = ldg16_nt(wp[j][1] + bo);
-      if constexpr (W4) {
-        const int gi = kb / 32 + 2 * (lane & 3);
+      if constexpr (W4 && !SB) {
+        const int gi = kb / 32 + 2 * (lane >> 4);
         sl.st[j][0] = sp[j][min(gi, gmax)];
         sl.st[j][1] = sp[j][min(gi + 1, gmax)];
       }
@@ -118,40 +124,74 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
         const int R = 8 * h + (lane >> 3);
         *reinterpret_cast<uint4*>(wslot + j * 2048 + wr + ((R ^ (2 * wc)) & 15) * 16) = sl.w[j][h];
       }
-      if constexpr (W4)
-        *reinterpret_cast<uint32_t*>(sslot + j * 256 + (lane >> 2) * 16 + (lane & 3) * 4) =
+      if constexpr (W4 && !SB)
+        *reinterpret_cast<uint32_t*>(sslot + j * 256 + (lane & 15) * 16 + (lane >> 4) * 4) =
             (sl.st[j][0] & 0xFFFFu) | (sl.st[j][1] << 16);
+    }
+  };
+
+  // ---- bulk int4 steps (SB): lane (row lane%16, unit lane/16 % DEPTH) of
+  // the round of DEPTH units starting at unit u0; past the range: clamped
+  // onto the row's last 16 bytes, never used
+  const int su = (lane >> 4) & (DEPTH - 1);
+  const int spmax = k1 / 256 - 1;
+  uint4 sreg[NB];
+  auto sload = [&](int u0) {
+    if constexpr (SB) {
+      const int pc = min(k0 / 256 + u0 + su, spmax);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) sreg[j] = ldg16(sp[j] + 8 * pc);
+    }
+  };
+  auto swrite = [&]() {
+    if constexpr (SB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        *reinterpret_cast<uint4*>(sslot + (su * NB + j) * 256 + (lane & 15) * 16) = sreg[j];
     }
   };
 
   // ---- activation chunks. Loads are clamped and stay unmasked in
   // registers (masking them at load time would make the next instruction
   // wait for every load in flight); the mask is applied by the LDS write.
+  // qv[q]: this wave's share of piece q holds a valid row (uniform: the
+  // wave's first row is valid, and valid rows are a prefix). Only the
+  // W4A16 path skips the others (4x the activation traffic per weight
+  // byte); for fp8/int8 the branches cost more registers than they save.
   uint4 aset[2][kPer];
+  bool qv[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) qv[q] = !W4 || __builtin_amdgcn_readfirstlane(am[q]) != 0u;
+  auto aoff = [&](int q, int buf) {
+    const int pc = tid + 256 * q;
+    const int row = pc / kRowPieces, piece = pc % kRowPieces;
+    const int mb = row >> 4, rr = row & 15;
+    const int s = piece / (8 * ESZ), c = piece % (8 * ESZ);
+    int off;
+    if constexpr (W4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
+    else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ (2 * c)) & 15) * 16;
+    return buf * kBuf + (mb * 2 + s) * kBlk + off;
+  };
   auto aload = [&](int ci, uint4 (&dst)[kPer]) {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const int piece = (tid + 256 * q) % kRowPieces;
-      const int k = k0 + ci * 256 + piece * (16 / ESZ);
-      dst[q] = ldg16(ap[q] + (size_t)min(k, K - 16 / ESZ) * ESZ);
+      if (qv[q]) {
+        const int piece = (tid + 256 * q) % kRowPieces;
+        const int k = k0 + ci * 256 + piece * (16 / ESZ);
+        dst[q] = ldg16(ap[q] + (size_t)min(k, K - 16 / ESZ) * ESZ);
+      }
     }
   };
   auto awrite = [&](const uint4 (&src)[kPer], int ci, int buf) {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
-      const int pc = tid + 256 * q;
-      const int row = pc / kRowPieces, piece = pc % kRowPieces;
-      const int k = k0 + ci * 256 + piece * (16 / ESZ);
-      const uint32_t m = k < k1 ? am[q] : 0u;
-      const int mb = row >> 4, rr = row & 15;
-      const int s = piece / (8 * ESZ), c = piece % (8 * ESZ);
-      int off;
-      if constexpr (W4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
-      else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ (2 * c)) & 15) * 16;
-      uint4 v = src[q];
-      if constexpr (W4) v = perm_even_odd_bf16(v);  // the order of dequant8_eo
-      *reinterpret_cast<uint4*>(lds + buf * kBuf + (mb * 2 + s) * kBlk + off) =
-          make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+      if (qv[q]) {
+        const int piece = (tid + 256 * q) % kRowPieces;
+        const int k = k0 + ci * 256 + piece * (16 / ESZ);
+        const uint32_t m = k < k1 ? am[q] : 0u;
+        uint4 v = src[q];
+        *reinterpret_cast<uint4*>(lds + aoff(q, buf)) = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+      }
     }
   };
   const int rd0 = g * 256 + ((r ^ (2 * g)) & 15) * 16;
@@ -160,18 +200,19 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 
   // multiply the weight unit in the wave's slot (unit u) with the
   // activation chunk that holds it
-  auto compute = [&](int u) {
+  auto compute = [&](int u, int d) {
     const uint8_t* abase = lds + ((u / UPC) & 1) * kBuf;
     if constexpr (W4) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         uint4 cw[NB];
-        float st[NB];
+        Int4Step st[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           cw[j] = *reinterpret_cast<const uint4*>(wslot + j * 2048 + s * 1024 + g * 256 +
                                                   ((r ^ (2 * (4 * s + g))) & 15) * 16);
-          st[j] = bf16_f32(*reinterpret_cast<const uint16_t*>(sslot + j * 256 + r * 16 + (4 * s + g) * 2));
+          st[j] = int4_step(bf16_f32(*reinterpret_cast<const uint16_t*>(sslot + ((SB ? d : 0) * NB + j) * 256 +
+                                                                        r * 16 + (4 * s + g) * 2)));
         }
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -179,7 +220,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
           for (int j = 0; j < NB; ++j) {
             const uint32_t word = w == 0 ? cw[j].x : w == 1 ? cw[j].y : w == 2 ? cw[j].z : cw[j].w;
-            bf[j] = dequant8_eo(word, st[j], -8.0f * st[j]);
+            bf[j] = dequant8_mix(word, st[j]);
           }
           const int off = s * kBlk + w * 1024 + rdw + ((r ^ (4 * g + w)) & 15) * 16;
 #pragma unroll
@@ -216,13 +257,22 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
     }
   };
 
-  // ---- prologue: activation chunks 0 and 1 in registers, chunk 0 in LDS,
-  // the weight ring filled
+  // ---- prologue: steps of the first round, activation chunks 0 and 1 in
+  // registers, chunk 0 in LDS, padding rows of both buffers zeroed, the
+  // weight ring filled
+  sload(0);
   aload(0, aset[0]);
   aload(1, aset[1]);
   SkinnySlot<KIND, NB> ring[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) wload(ring[d], d);
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    if (!qv[q]) {
+      *reinterpret_cast<uint4*>(lds + aoff(q, 0)) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(lds + aoff(q, 1)) = make_uint4(0, 0, 0, 0);
+    }
+  }
   awrite(aset[0], 0, 0);
   __syncthreads();
 
@@ -233,17 +283,23 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   // slot is refilled DEPTH units ahead (past the range: clamped loads of
   // valid memory, never used), then the unit is multiplied. The scheduling
   // barriers keep each refill right after the write that freed its slot.
+  // With SB the round's steps go to the step slot first and the next
+  // round's are loaded (the step slot is read only by this wave, in order).
   const int full = nunits / DEPTH, rem = nunits % DEPTH;
   for (int rd = 0; rd < full; ++rd) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int u = rd * DEPTH + d;
       if (d % UPC == 0) aload(u / UPC + 2, aset[(d / UPC) & 1]);
+      if (d == 0) {
+        swrite();
+        sload(u + DEPTH);
+      }
       wstage(ring[d]);
       __builtin_amdgcn_sched_barrier(0);
       wload(ring[d], u + DEPTH);
       __builtin_amdgcn_sched_barrier(0);
-      compute(u);
+      compute(u, d);
       if (d % UPC == UPC - 1) {
         awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
         __syncthreads();
@@ -251,14 +307,16 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
     }
   }
   // ---- the last rem units are already in the ring; the activation chunks
-  // continue as above. The condition is uniform over the workgroup.
+  // continue as above (their steps are in sreg). The condition is uniform
+  // over the workgroup.
+  if (rem > 0) swrite();
 #pragma unroll
   for (int d = 0; d < DEPTH - 1; ++d) {
     if (d < rem) {
       const int u = full * DEPTH + d;
       if (d % UPC == 0) aload(u / UPC + 2, aset[(d / UPC) & 1]);
       wstage(ring[d]);
-      compute(u);
+      compute(u, d);
       if (d % UPC == UPC - 1 && d + 1 < rem) {
         awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
         __syncthreads();

@@ -217,6 +217,7 @@ GEMM_CASES = [
     ("c1", 1, None, None, (4, 1, 3)),
     ("ragged", 1, 48, 288, (5, 17, 33, 50)),
     ("c2", 2, None, None, (1, 8, 64)),
+    ("k512", 1, 80, 512, (17, 33)),
     ("prefill_small", 1, 160, 416, (65, 130, 200)),
     # enough 256x256 tiles for the persistent kernel, with ragged M, N and K tails
     ("prefill_big_ragged", 1, 4112, 416, (2000,)),
@@ -234,6 +235,22 @@ def test_gemm_full_outputs(q, oracle, fmt, case):
         g32 = host(_gpu_gemm(q, fmt, ops, M, torch.float32))
         g16 = host(_gpu_gemm(q, fmt, ops, M, torch.bfloat16))
         _compare(fmt, g32, g16, y32, y16, f"{fmt} {name} M={M} N={d['N']} K={d['K']}")
+
+
+def test_gemm_w4a16_unaligned_steps(q, oracle):
+    """Step rows that are not 16-byte aligned (K % 256 == 0 but the step
+    pointer 2 bytes past an aligned address) take the per-unit step loads."""
+    d = gen.linear_config(1, n=96, k=512, m=40)
+    ops = _operands(oracle, d, "w4a16")
+    s = dev(ops["steps"])
+    buf = torch.empty(s.numel() + 8, dtype=s.dtype, device=s.device)
+    sv = buf[1:1 + s.numel()].view(s.shape)
+    sv.copy_(s)
+    assert sv.data_ptr() % 16 != 0
+    for M in (1, 17, 40):
+        y32, _ = _oracle_gemm(oracle, "w4a16", ops, M)
+        g = host(q.gemm_w4a16(dev(ops["a"][:M]), dev(ops["packed"]), sv, out_dtype=torch.float32))
+        tol_check(g, y32, f"w4a16 unaligned steps M={M}")
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8", "w4a16"])
