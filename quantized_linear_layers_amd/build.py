@@ -20,6 +20,10 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-ffp-contract=off",  # every fused multiply-add is written out explicitly
+    # LDS slots are written and read through different pointer types by
+    # different lanes of one wave (ordered by the hardware, not by barriers):
+    # type-based alias analysis must not reorder those accesses
+    "-fno-strict-aliasing",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-function",

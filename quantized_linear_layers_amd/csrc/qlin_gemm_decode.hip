@@ -225,25 +225,22 @@ static int decode_cus() {
   return cus;
 }
 
-// Per-kind tile shape: a wave takes two column blocks once the activation
-// fragments it reads per weight byte would otherwise dominate (MB >= 3).
-static int decode_nb(int kind, int MB) {
-  if (kind == kGemmW4) return MB >= 2 ? 2 : 1;
-  return MB >= 3 ? 2 : 1;
-}
-
-// Grid: 64*NB columns per workgroup, S splits of K. Split-K costs a write
-// and a read of S*M*N partial sums, so it is used only to reach about three
-// quarters of the CUs with column tiles; each split keeps >= 4 steps of
-// 128 K.
+// Grid: 64*NB columns per workgroup, S splits of K. A wave takes one
+// 16-column block, or two at MB >= 3 (half the activation fragments read
+// per weight byte) when the 128-column tiles alone reach about three
+// quarters of the CUs. Split-K costs a write and a read of S*M*N partial
+// sums, so it is used only to reach that many workgroups (W4A16 with one
+// block above 16 rows, bound by its unpack and MFMA issue rather than by
+// HBM, wants two per CU); each split keeps >= 4 steps of 128 K.
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
+  const int64_t cus = decode_cus();
   c.MB = (int)((M + 15) / 16);
-  c.NB = decode_nb(kind, c.MB);
+  c.NB = c.MB >= 3 && (N + 127) / 128 >= 3 * cus / 4 ? 2 : 1;
   const int64_t cols = (int64_t)64 * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
-  const int64_t want = 3 * (int64_t)decode_cus() / 4;
+  const int64_t want = kind == kGemmW4 && c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
   int64_t S = (want + c.tiles - 1) / c.tiles;
   S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
   if (const char* e = getenv("QLIN_DECODE_SPLIT")) S = std::max(1, atoi(e));  // tuning override
@@ -255,29 +252,29 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   return c;
 }
 
-// Dispatch on (kind, MB, bulk steps) to the instantiation that serves it.
-// DEPTH (weight units in flight per wave) per (kind, MB), as measured: 8
-// fp8/int8 128-K units at MB <= 2, 4 above; int4 256-K units: 2 at MB = 1
-// (deeper rings were slower), 4 at MB = 2, 2 above (register bound).
+// Dispatch on (kind, MB, NB, bulk steps) to the instantiation that serves
+// it. DEPTH (weight units in flight per wave), as measured: 4 fp8/int8
+// 128-K units (8 was slower); int4 256-K units: 2 at MB = 1 and with two
+// blocks (register bound), 4 otherwise.
 template <typename F>
-static auto with_decode_inst(int kind, int MB, bool sb, F&& f) {
-#define QLIN_DEC(K, NB1, NB2, D1, D2, D3, SB)                 \
-  switch (MB) {                                              \
-    case 1: return f.template operator()<K, 1, NB1, D1, SB>(); \
-    case 2: return f.template operator()<K, 2, NB2, D2, SB>(); \
-    case 3: return f.template operator()<K, 3, 2, D3, SB>();   \
-    default: return f.template operator()<K, 4, 2, D3, SB>();  \
+static auto with_decode_inst(int kind, int MB, int NB, bool sb, F&& f) {
+#define QLIN_DEC(K, D1, D2, D22, SB)                                                          \
+  switch (MB) {                                                                              \
+    case 1: return f.template operator()<K, 1, 1, D1, SB>();                                   \
+    case 2: return f.template operator()<K, 2, 1, D2, SB>();                                   \
+    case 3: return NB == 2 ? f.template operator()<K, 3, 2, D22, SB>() : f.template operator()<K, 3, 1, D2, SB>(); \
+    default: return NB == 2 ? f.template operator()<K, 4, 2, D22, SB>() : f.template operator()<K, 4, 1, D2, SB>(); \
   }
   if (kind == kGemmW4) {
     if (sb) {
-      QLIN_DEC(kGemmW4, 1, 2, 2, 4, 2, true)
+      QLIN_DEC(kGemmW4, 2, 4, 2, true)
     } else {
-      QLIN_DEC(kGemmW4, 1, 2, 2, 4, 2, false)
+      QLIN_DEC(kGemmW4, 2, 4, 2, false)
     }
   } else if (kind == kGemmI8) {
-    QLIN_DEC(kGemmI8, 1, 1, 8, 8, 4, false)
+    QLIN_DEC(kGemmI8, 4, 4, 4, false)
   } else {
-    QLIN_DEC(kGemmFP8, 1, 1, 8, 8, 4, false)
+    QLIN_DEC(kGemmFP8, 4, 4, 4, false)
   }
 #undef QLIN_DEC
 }
@@ -329,7 +326,7 @@ int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const v
   }
   // int4 steps in 16-byte pieces of 8 groups: aligned rows, whole pieces
   const bool sb = kind == kGemmW4 && K % 256 == 0 && ((uintptr_t)wsc & 15) == 0;
-  with_decode_inst(kind, c.MB, sb, LaunchFn{&g, &c, st});
+  with_decode_inst(kind, c.MB, c.NB, sb, LaunchFn{&g, &c, st});
   return launch_status();
 }
 
