@@ -257,8 +257,10 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
 // Global loads: one instruction covers 8 rows x 128 contiguous bytes (whole
 // cache lines). LDS keeps every 16-row block "fragment-major": the 16-byte
 // piece that MFMA lane (g, r) needs for K half h (chunk c = 4h + g of row r)
-// sits at h*1024 + g*256 + 16*(r ^ 2c), so both the fragment reads and the
-// line-shaped staging writes hit distinct banks.
+// sits at h*1024 + g*256 + 16*((r ^ c) & 15), so both the fragment reads
+// (16 lanes of one chunk, r = 0..15) and the line-shaped staging writes (8
+// lanes per 128-byte write cycle holding chunks c = 0..7 of one row) hit
+// distinct banks.
 // The MFMA takes the W block as its first operand, so each lane ends with 4
 // consecutive output columns of one row: the epilogue stores 8 (bf16) or 16
 // (fp32) bytes per lane per block. The next tile's first loads are issued
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(WM * WN * 64) void prefill_gemm_kernel(const Prefil
 // Tiles are visited in grouped order, and each round of the workgroups hands
 // every XCD a compact block of tiles (workgroups are dispatched round-robin
 // over the XCDs), so tiles that share A rows or W rows share an L2.
-template <int KIND>
+template <int KIND, bool KTAIL>
 __global__ __launch_bounds__(256) void prefill_big_kernel(const PrefillArgs p, int tiles_m,
                                                           int tiles_n) {
   constexpr int kStage = 65536, kWOff = 32768;
@@ -288,9 +290,9 @@ __global__ __launch_bounds__(256) void prefill_big_kernel(const PrefillArgs p, i
   const int c = lane & 7;
   const int srow = 8 * wave + (lane >> 3);
   const int kofs = 16 * c;
-  const int wr_off = (wave >> 1) * 2048 + (c >> 2) * 1024 + (c & 3) * 256 + (((srow & 15) ^ (2 * c)) * 16);
-  const int rd0 = g * 256 + ((r ^ (2 * g)) * 16);
-  const int rd1 = 1024 + g * 256 + ((r ^ (2 * (4 + g))) * 16);
+  const int wr_off = (wave >> 1) * 2048 + (c >> 2) * 1024 + (c & 3) * 256 + (((srow & 15) ^ c) * 16);
+  const int rd0 = g * 256 + ((r ^ g) * 16);
+  const int rd1 = 1024 + g * 256 + ((r ^ (4 + g)) * 16);
   const int ra = wm * 16384, rb = kWOff + wn * 16384;
 
   uint4 st[16];
@@ -305,20 +307,27 @@ __global__ __launch_bounds__(256) void prefill_big_kernel(const PrefillArgs p, i
     m0 = (first_m + (t % per_group) % gsz) * 256;
     n0 = ((t % per_group) / gsz) * 256;
   };
+  // Staging addresses: 32-bit byte offsets from the uniform matrix base (the
+  // launch checks that M*lda and N*K fit), the row clamp applied to the
+  // offset (rows are lda / K bytes apart), then the clamped K chunk.
+  const uint32_t lda = (uint32_t)p.lda, ldw = (uint32_t)p.K;
+  const uint32_t arow = (uint32_t)srow * lda, wrow = (uint32_t)srow * ldw;
+  const uint32_t amax = (uint32_t)(p.M - 1) * lda, wmax = (uint32_t)(p.N - 1) * ldw;
   auto gload_one = [&](int q, int kt, int m0, int n0) {
-    const int kc = min(kt * 128 + kofs, p.K - 16);
+    const uint32_t kc = (uint32_t)min(kt * 128 + kofs, p.K - 16);
     if (q < 8) {
-      const int m = min(m0 + srow + 32 * q, p.M - 1);
-      st[q] = ldg16(p.A + (size_t)m * p.lda + kc);
+      const uint32_t o = min((uint32_t)m0 * lda + (uint32_t)(32 * q) * lda + arow, amax) + kc;
+      st[q] = ldg16(p.A + o);
     } else {
-      const int n = min(n0 + srow + 32 * (q - 8), p.N - 1);
-      st[q] = ldg16(p.W + (size_t)n * p.K + kc);
+      const uint32_t o = min((uint32_t)n0 * ldw + (uint32_t)(32 * (q - 8)) * ldw + wrow, wmax) + kc;
+      st[q] = ldg16(p.W + o);
     }
   };
-  // LDS write of staging slot q (stage kt) into buffer `buf`; A chunks past K are zeroed
+  // LDS write of staging slot q (stage kt) into buffer `buf`; A chunks past K
+  // are zeroed (only when K is not a multiple of 128)
   auto swrite = [&](int q, int kt, int buf) {
     uint4 v = st[q];
-    if (q < 8) {
+    if (KTAIL && q < 8) {
       const uint32_t keep = kt * 128 + kofs < p.K ? 0xFFFFFFFFu : 0u;
       v = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
@@ -511,7 +520,8 @@ template <int KIND>
 static void launch_prefill_big(const PrefillArgs& a, hipStream_t st) {
   const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
   const int grid = std::min(tm * tn, device_cus());
-  prefill_big_kernel<KIND><<<dim3((unsigned)grid), 256, 0, st>>>(a, tm, tn);
+  if (a.K % 128 == 0) prefill_big_kernel<KIND, false><<<dim3((unsigned)grid), 256, 0, st>>>(a, tm, tn);
+  else prefill_big_kernel<KIND, true><<<dim3((unsigned)grid), 256, 0, st>>>(a, tm, tn);
 }
 
 int launch_prefill(int kind, const void* a, int64_t lda, const float* sa, const void* w,
@@ -531,7 +541,9 @@ int launch_prefill(int kind, const void* a, int64_t lda, const float* sa, const 
   g.out_f32 = out_f32;
   // enough 256x256 tiles to occupy half the device or more: the persistent
   // pipelined kernel; otherwise 128x128 tiles so the grid still fills it
-  const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= device_cus() / 2;
+  // (its staging offsets are 32-bit: both operands under 2 GiB)
+  const bool big = ((M + 255) / 256) * ((N + 255) / 256) >= device_cus() / 2 &&
+                   (uint64_t)M * (uint64_t)lda < (1ull << 31) && (uint64_t)N * (uint64_t)K < (1ull << 31);
   if (kind == kGemmFP8) {
     if (big) launch_prefill_big<kGemmFP8>(g, st);
     else launch_prefill_t<kGemmFP8, 128, 128, 2, 2>(g, st);

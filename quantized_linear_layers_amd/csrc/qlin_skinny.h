@@ -15,15 +15,19 @@
 //    from which the MFMA fragments are read (LDS operations of one wave
 //    complete in order, so that slot needs no barrier);
 //  * LDS blocks are "fragment-major": the 16 bytes that MFMA lane (r, g)
-//    reads for one operand piece sit at piece*1024 + g*256 + 16*(r ^ f(c)),
-//    c being the 16-byte chunk of the row segment; the XOR spreads the
-//    line-shaped staging writes over the banks.
+//    reads for one operand piece sit at piece*1024 + g*256 + 16*((r ^ c) & 15),
+//    c being the 16-byte chunk of the row segment. The XOR keeps both access
+//    shapes free of bank conflicts: a 16-byte LDS write is serviced 8 lanes
+//    (128 bytes) at a time, and the 8 lanes of one staging write hold chunks
+//    c = 0..7 of one row, so (r ^ c) & 7 takes 8 distinct values (r ^ 2c
+//    would take 4: a 2-way conflict); the 16 lanes of a fragment read share
+//    c and cover r = 0..15.
 //      fp8 / int8 (2 KB per 16-row block and 128-K step): piece = K half h,
-//        chunk c = 4h + g, f = 2c; weights use the same layout;
+//        chunk c = 4h + g; weights use the same layout;
 //      int4 weights (2 KB per block and unit of two steps): piece = step s,
-//        chunk c = 4s + g (the 32 codes of group 4s + g), f = 2c;
+//        chunk c = 4s + g (the 32 codes of group 4s + g);
 //      bf16 activations (4 KB per block and step): piece = MFMA w of the
-//        step, chunk c = 4g + w (values k = 32g + 8w .. +8), f = c.
+//        step, chunk c = 4g + w (values k = 32g + 8w .. +8).
 //  * int4 group steps: with SB (16-byte aligned step rows, K % 256 == 0)
 //    one 16-byte load per lane fetches the steps of 16 rows x DEPTH units
 //    once per round of DEPTH units, into a wave-private LDS slot of DEPTH
@@ -122,7 +126,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int R = 8 * h + (lane >> 3);
-        *reinterpret_cast<uint4*>(wslot + j * 2048 + wr + ((R ^ (2 * wc)) & 15) * 16) = sl.w[j][h];
+        *reinterpret_cast<uint4*>(wslot + j * 2048 + wr + ((R ^ wc) & 15) * 16) = sl.w[j][h];
       }
       if constexpr (W4 && !SB)
         *reinterpret_cast<uint32_t*>(sslot + j * 256 + (lane & 15) * 16 + (lane >> 4) * 4) =
@@ -169,7 +173,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
     const int s = piece / (8 * ESZ), c = piece % (8 * ESZ);
     int off;
     if constexpr (W4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
-    else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ (2 * c)) & 15) * 16;
+    else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ c) & 15) * 16;
     return buf * kBuf + (mb * 2 + s) * kBlk + off;
   };
   auto aload = [&](int ci, uint4 (&dst)[kPer]) {
@@ -194,8 +198,8 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
       }
     }
   };
-  const int rd0 = g * 256 + ((r ^ (2 * g)) & 15) * 16;
-  const int rd1 = 1024 + g * 256 + ((r ^ (2 * (4 + g))) & 15) * 16;
+  const int rd0 = g * 256 + ((r ^ g) & 15) * 16;
+  const int rd1 = 1024 + g * 256 + ((r ^ (4 + g)) & 15) * 16;
   const int rdw = g * 256;
 
   // multiply the weight unit in the wave's slot (unit u) with the
@@ -210,7 +214,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           cw[j] = *reinterpret_cast<const uint4*>(wslot + j * 2048 + s * 1024 + g * 256 +
-                                                  ((r ^ (2 * (4 * s + g))) & 15) * 16);
+                                                  ((r ^ (4 * s + g)) & 15) * 16);
           st[j] = int4_step(bf16_f32(*reinterpret_cast<const uint16_t*>(sslot + ((SB ? d : 0) * NB + j) * 256 +
                                                                         r * 16 + (4 * s + g) * 2)));
         }
