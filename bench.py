@@ -463,7 +463,7 @@ def cpu_baseline(gen, d, Ms, step_weight_bytes, budget_s=12.0):
     t0 = time.perf_counter()
     one()
     reps = 1
-    while time.perf_counter() - t0 < budget_s and reps < 20:
+    while time.perf_counter() - t0 < budget_s and reps < 1000:
         one()
         reps += 1
     dt = time.perf_counter() - t0
