@@ -55,13 +55,13 @@ struct GemmArgs {
 // Decode-shaped GEMM: the streaming core of qlin_skinny.h over this
 // workgroup's 64*NB columns and this split's K range, then the split-K
 // reduction and the epilogue.
-template <int KIND, int MB, int NB, int DEPTH, bool SB>
-__global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
+template <int KIND, int MB, int NB, int DEPTH, bool SB, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) {
   using Acc = SkinnyAcc<KIND>;
   constexpr bool W4 = KIND == kGemmW4;
   constexpr int ESZ = W4 ? 2 : 1;
-  constexpr int kPer = MB * ESZ;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<KIND, MB, NB, DEPTH>()];
+  constexpr int kPer = skinny_pieces<KIND, MB, NW>();
+  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<KIND, MB, NB, DEPTH, NW>()];
   __shared__ unsigned last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   const int r = lane & 15, g = lane >> 4;
   const int split = blockIdx.y, S = gridDim.y;
   const int k0 = split * p.kc, k1 = min(k0 + p.kc, p.K);
-  const int n0 = (blockIdx.x * 4 + wave) * 16 * NB;  // this wave's first column
+  const int n0 = (blockIdx.x * NW + wave) * 16 * NB;  // this wave's first column
 
   // operand rows (clamped onto valid rows; padding activation rows masked)
   const uint8_t* wp[NB][2];
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   uint32_t am[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    const int row = (tid + 256 * q) / (16 * ESZ);
+    const int row = (tid + 64 * NW * q) / (16 * ESZ);
     ap[q] = p.A + (size_t)min(row, p.M - 1) * p.lda * ESZ;
     am[q] = row < p.M ? 0xFFFFFFFFu : 0u;
   }
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
-  skinny_mma<KIND, MB, NB, DEPTH, SB>(lds, wp, sp, ap, am, p.K, k0, k1, acc);
+  skinny_mma<KIND, MB, NB, DEPTH, SB, NW>(lds, wp, sp, ap, am, p.K, k0, k1, acc);
 
   // ---- split-K: publish partials, the last workgroup of the tile reduces
   float accf[MB][NB][4];
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void decode_gemm_kernel(const GemmArgs p) {
 // launch configuration
 // ----------------------------------------------------------------------------
 struct DecodeCfg {
-  int MB, NB;
+  int MB, NB, NW;
   int tiles, S, kc;
 };
 
@@ -237,7 +237,8 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   const int64_t cus = decode_cus();
   c.MB = (int)((M + 15) / 16);
   c.NB = c.MB >= 3 && (N + 127) / 128 >= 3 * cus / 4 ? 2 : 1;
-  const int64_t cols = (int64_t)64 * c.NB;
+  c.NW = kind == kGemmW4 && c.NB == 2 ? 8 : 4;
+  const int64_t cols = (int64_t)16 * c.NW * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
   const int64_t want = kind == kGemmW4 && c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
@@ -255,26 +256,29 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
 // Dispatch on (kind, MB, NB, bulk steps) to the instantiation that serves
 // it. DEPTH (weight units in flight per wave), as measured: 4 fp8/int8
 // 128-K units (8 was slower); int4 256-K units: 2 at MB = 1 and with two
-// blocks (register bound), 4 otherwise.
+// blocks (register bound), 4 otherwise. W4A16 with two blocks per wave runs
+// 8 waves per workgroup (two per SIMD: one wave's unpack hides the other's
+// waits; K=5120, N=25600, M=64: 43.7 instead of 52.4 us; with one block
+// per wave, or fp8/int8, 8 waves measured no better).
 template <typename F>
 static auto with_decode_inst(int kind, int MB, int NB, bool sb, F&& f) {
-#define QLIN_DEC(K, D1, D2, D22, SB)                                                          \
+#define QLIN_DEC(K, D1, D2, D22, NW2, SB)                                                          \
   switch (MB) {                                                                              \
-    case 1: return f.template operator()<K, 1, 1, D1, SB>();                                   \
-    case 2: return f.template operator()<K, 2, 1, D2, SB>();                                   \
-    case 3: return NB == 2 ? f.template operator()<K, 3, 2, D22, SB>() : f.template operator()<K, 3, 1, D2, SB>(); \
-    default: return NB == 2 ? f.template operator()<K, 4, 2, D22, SB>() : f.template operator()<K, 4, 1, D2, SB>(); \
+    case 1: return f.template operator()<K, 1, 1, D1, SB, 4>();                                \
+    case 2: return f.template operator()<K, 2, 1, D2, SB, 4>();                                \
+    case 3: return NB == 2 ? f.template operator()<K, 3, 2, D22, SB, NW2>() : f.template operator()<K, 3, 1, D2, SB, 4>(); \
+    default: return NB == 2 ? f.template operator()<K, 4, 2, D22, SB, NW2>() : f.template operator()<K, 4, 1, D2, SB, 4>(); \
   }
   if (kind == kGemmW4) {
     if (sb) {
-      QLIN_DEC(kGemmW4, 2, 4, 2, true)
+      QLIN_DEC(kGemmW4, 2, 4, 2, 8, true)
     } else {
-      QLIN_DEC(kGemmW4, 2, 4, 2, false)
+      QLIN_DEC(kGemmW4, 2, 4, 2, 8, false)
     }
   } else if (kind == kGemmI8) {
-    QLIN_DEC(kGemmI8, 4, 4, 4, false)
+    QLIN_DEC(kGemmI8, 4, 4, 4, 4, false)
   } else {
-    QLIN_DEC(kGemmFP8, 4, 4, 4, false)
+    QLIN_DEC(kGemmFP8, 4, 4, 4, 4, false)
   }
 #undef QLIN_DEC
 }
@@ -295,9 +299,9 @@ struct LaunchFn {
   const GemmArgs* a;
   const DecodeCfg* c;
   hipStream_t st;
-  template <int KIND, int MB, int NB, int DEPTH, bool SB>
+  template <int KIND, int MB, int NB, int DEPTH, bool SB, int NW>
   int operator()() const {
-    decode_gemm_kernel<KIND, MB, NB, DEPTH, SB><<<dim3((unsigned)c->tiles, (unsigned)c->S), 256, 0, st>>>(*a);
+    decode_gemm_kernel<KIND, MB, NB, DEPTH, SB, NW><<<dim3((unsigned)c->tiles, (unsigned)c->S), 64 * NW, 0, st>>>(*a);
     return 0;
   }
 };

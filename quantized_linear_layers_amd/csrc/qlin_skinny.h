@@ -1,10 +1,10 @@
 // Streaming core of the weight-bound ("skinny", M <= 64 rows) quantized
 // GEMMs of libqlin: the dense decode GEMMs and the MoE expert GEMMs.
 //
-// A workgroup of 4 waves computes an (MB*16) x (4 * NB*16) output tile over
-// one K range [k0, k1):
+// A workgroup of NW waves (4 or 8) computes an (MB*16) x (NW * NB*16) output
+// tile over one K range [k0, k1):
 //  * activations pass through LDS in chunks of 256 K, double buffered and
-//    shared by the 4 waves (one barrier per chunk), fetched once per
+//    shared by the NW waves (one barrier per chunk), fetched once per
 //    workgroup in whole cache lines; K past the range is zeroed when
 //    written; rows past the valid count are zeroed once, and waves whose
 //    share of a chunk holds no valid row skip its loads and writes;
@@ -49,10 +49,16 @@ namespace qlin {
 template <int KIND>
 using SkinnyAcc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
 
-// Per-workgroup LDS bytes of skinny_mma<KIND, MB, NB, DEPTH>.
-template <int KIND, int MB, int NB, int DEPTH>
+// Per-workgroup LDS bytes of skinny_mma<KIND, MB, NB, DEPTH, SB, NW>.
+template <int KIND, int MB, int NB, int DEPTH, int NW = 4>
 constexpr int skinny_lds_bytes() {
-  return 2 * MB * 2 * 16 * 128 * (KIND == kGemmW4 ? 2 : 1) + 4 * NB * (2048 + (KIND == kGemmW4 ? 256 * DEPTH : 0));
+  return 2 * MB * 2 * 16 * 128 * (KIND == kGemmW4 ? 2 : 1) + NW * NB * (2048 + (KIND == kGemmW4 ? 256 * DEPTH : 0));
+}
+
+// Activation pieces (16 bytes) each of the 64*NW threads stages per chunk.
+template <int KIND, int MB, int NW>
+constexpr int skinny_pieces() {
+  return MB * (KIND == kGemmW4 ? 2 : 1) * 4 / NW;
 }
 
 // One weight unit of one wave in registers.
@@ -72,14 +78,14 @@ struct SkinnySlot<kGemmW4, NB> {
 //  sp[j]     int4 group steps of tile row lane%16 of block j (W4A16 only);
 //  wbytes    weight bytes per row (K or K/2);
 //  ap[q]     activation row of this thread's chunk piece q (row
-//            (tid + 256q) / (16 * ESZ) of the tile; clamped onto a valid row)
+//            (tid + 64*NW*q) / (16 * ESZ) of the tile; clamped onto a valid row)
 //  am[q]     0xFFFFFFFF if that row is a real row, else 0 (the real rows
 //            must be a prefix of the tile's rows);
 //  K         full K (clamps the activation loads), k0/k1 the range.
-template <int KIND, int MB, int NB, int DEPTH, bool SB = false>
+template <int KIND, int MB, int NB, int DEPTH, bool SB = false, int NW = 4>
 __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB][2], const uint16_t* (&sp)[NB],
-                                           const uint8_t* (&ap)[MB * (KIND == kGemmW4 ? 2 : 1)],
-                                           uint32_t (&am)[MB * (KIND == kGemmW4 ? 2 : 1)], int K, int k0,
+                                           const uint8_t* (&ap)[skinny_pieces<KIND, MB, NW>()],
+                                           uint32_t (&am)[skinny_pieces<KIND, MB, NW>()], int K, int k0,
                                            int k1, SkinnyAcc<KIND> (&acc)[MB][NB]) {
   constexpr bool W4 = KIND == kGemmW4;
   constexpr int ESZ = W4 ? 2 : 1;                    // activation bytes per element
@@ -89,7 +95,9 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   constexpr int kBlk = 16 * 128 * ESZ;               // LDS bytes per (mb, step) of activations
   constexpr int kBuf = MB * 2 * kBlk;                // one 256-K activation chunk
   constexpr int kRowPieces = 16 * ESZ;               // 16-byte pieces per row per chunk
-  constexpr int kPer = MB * ESZ;                     // activation pieces per thread per chunk
+  constexpr int NT = 64 * NW;                        // threads of the workgroup
+  constexpr int kPer = skinny_pieces<KIND, MB, NW>();  // activation pieces per thread per chunk
+  static_assert(kPer * NW == MB * ESZ * 4 && kPer >= 1, "activation chunk split over the threads");
   constexpr int kWSlot = NB * 2048;                  // one wave's weight unit in LDS
   constexpr int kSSlot = W4 ? DEPTH * NB * 256 : 0;  // ... and its int4 group steps
   static_assert(!SB || (W4 && DEPTH <= 4), "bulk steps: W4A16, one load covers <= 4 units");
@@ -99,7 +107,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   const int r = lane & 15, g = lane >> 4;
   const int nunits = (k1 - k0 + kUnitK - 1) / kUnitK;
   uint8_t* wslot = lds + 2 * kBuf + wave * kWSlot;
-  uint8_t* sslot = lds + 2 * kBuf + 4 * kWSlot + wave * kSSlot;
+  uint8_t* sslot = lds + 2 * kBuf + NW * kWSlot + wave * kSSlot;
 
   // ---- weights
   const int wc = lane & 7;
@@ -167,7 +175,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
   for (int q = 0; q < kPer; ++q) qv[q] = !W4 || __builtin_amdgcn_readfirstlane(am[q]) != 0u;
   auto aoff = [&](int q, int buf) {
-    const int pc = tid + 256 * q;
+    const int pc = tid + NT * q;
     const int row = pc / kRowPieces, piece = pc % kRowPieces;
     const int mb = row >> 4, rr = row & 15;
     const int s = piece / (8 * ESZ), c = piece % (8 * ESZ);
@@ -180,7 +188,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       if (qv[q]) {
-        const int piece = (tid + 256 * q) % kRowPieces;
+        const int piece = (tid + NT * q) % kRowPieces;
         const int k = k0 + ci * 256 + piece * (16 / ESZ);
         dst[q] = ldg16(ap[q] + (size_t)min(k, K - 16 / ESZ) * ESZ);
       }
@@ -190,7 +198,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       if (qv[q]) {
-        const int piece = (tid + 256 * q) % kRowPieces;
+        const int piece = (tid + NT * q) % kRowPieces;
         const int k = k0 + ci * 256 + piece * (16 / ESZ);
         const uint32_t m = k < k1 ? am[q] : 0u;
         uint4 v = src[q];

@@ -237,6 +237,17 @@ def test_gemm_full_outputs(q, oracle, fmt, case):
         _compare(fmt, g32, g16, y32, y16, f"{fmt} {name} M={M} N={d['N']} K={d['K']}")
 
 
+def test_gemm_w4a16_wide_ragged_k(q, oracle):
+    """N wide enough for two column blocks per wave (8 waves per workgroup
+    for W4A16) with K % 256 != 0 (per-unit step loads), M = 40 and 64."""
+    d = gen.linear_config(1, n=24576, k=288, m=64)
+    ops = _operands(oracle, d, "w4a16")
+    for M in (40, 64):
+        y32, _ = _oracle_gemm(oracle, "w4a16", ops, M)
+        g = host(_gpu_gemm(q, "w4a16", ops, M, torch.float32))
+        tol_check(g, y32, f"w4a16 wide ragged-K M={M}")
+
+
 def test_gemm_w4a16_unaligned_steps(q, oracle):
     """Step rows that are not 16-byte aligned (K % 256 == 0 but the step
     pointer 2 bytes past an aligned address) take the per-unit step loads."""
@@ -293,7 +304,7 @@ def c3ops(oracle):
 def test_gemm_c3_full_size_sampled(q, oracle, c3ops, fmt):
     ops = c3ops[fmt]
     rng = np.random.default_rng(17)
-    for M in (1, 8, 64):
+    for M in (1, 8, 40, 64):
         g = host(_gpu_gemm(q, fmt, ops, M, torch.float32))
         mi, ni = _sampled(rng, M, g.shape[1], 3000)
         ref = _oracle_sample(oracle, fmt, ops, M, mi, ni)
