@@ -225,10 +225,12 @@ static int decode_cus() {
   return cus;
 }
 
-// Grid: 64*NB columns per workgroup, S splits of K. A wave takes one
-// 16-column block, or two at MB >= 3 (half the activation fragments read
-// per weight byte) when the 128-column tiles alone reach about three
-// quarters of the CUs. Split-K costs a write and a read of S*M*N partial
+// Grid: 16*NB*NW columns per workgroup, S splits of K. A wave takes one
+// 16-column block, or two when the 128-column tiles alone reach about three
+// quarters of the CUs (fp8/int8 at any M: more bytes in flight per wave,
+// K=5120, N=25600: 22.7 instead of 23.6 us at M = 1; W4A16 from MB = 3,
+// where it halves the activation fragments read per weight byte; at M <= 16
+// it was slower). Split-K costs a write and a read of S*M*N partial
 // sums, so it is used only to reach that many workgroups (W4A16 with one
 // block above 16 rows, bound by its unpack and MFMA issue rather than by
 // HBM, wants two per CU); each split keeps >= 4 steps of 128 K.
@@ -236,7 +238,7 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   const int64_t cus = decode_cus();
   c.MB = (int)((M + 15) / 16);
-  c.NB = c.MB >= 3 && (N + 127) / 128 >= 3 * cus / 4 ? 2 : 1;
+  c.NB = (kind != kGemmW4 || c.MB >= 3) && (N + 127) / 128 >= 3 * cus / 4 ? 2 : 1;
   c.NW = kind == kGemmW4 && c.NB == 2 ? 8 : 4;
   const int64_t cols = (int64_t)16 * c.NW * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
@@ -264,8 +266,12 @@ template <typename F>
 static auto with_decode_inst(int kind, int MB, int NB, bool sb, F&& f) {
 #define QLIN_DEC(K, D1, D2, D22, NW2, SB)                                                          \
   switch (MB) {                                                                              \
-    case 1: return f.template operator()<K, 1, 1, D1, SB, 4>();                                \
-    case 2: return f.template operator()<K, 2, 1, D2, SB, 4>();                                \
+    case 1:                                                                                  \
+      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 1, 2, D2, SB, 4>(); \
+      return f.template operator()<K, 1, 1, D1, SB, 4>();                                    \
+    case 2:                                                                                  \
+      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 2, 2, D2, SB, 4>(); \
+      return f.template operator()<K, 2, 1, D2, SB, 4>();                                    \
     case 3: return NB == 2 ? f.template operator()<K, 3, 2, D22, SB, NW2>() : f.template operator()<K, 3, 1, D2, SB, 4>(); \
     default: return NB == 2 ? f.template operator()<K, 4, 2, D22, SB, NW2>() : f.template operator()<K, 4, 1, D2, SB, 4>(); \
   }
