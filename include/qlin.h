@@ -197,7 +197,11 @@ int qlin_gemm_w8a8(const int8_t* a_q, const float* a_scale, const int8_t* w_q,
  * 4-Bit Builds Stay Slow": TritonW4A16LinearKernel unpacks the weights to
  * bf16 before each multiply; [E2B]: the card has no int4 multiply):
  *   Y[m,n] = sum_k a[m,k] * bf16(c[n,k] * step[n,k/32]), fp32 accumulation.
- *   a [M][lda] bf16 (lda % 8 == 0); codes/steps as from qlin_repack_q4_0. */
+ *   a [M][lda] bf16 (lda % 8 == 0); codes/steps as from qlin_repack_q4_0.
+ *   Steps must be finite with magnitude below 2^117 (the unpack computes
+ *   c*step as (1024 + u)*step - 1032*step; larger steps overflow to inf;
+ *   q4_0 steps are fp16 values, far below this). K % 32 == 0; the fastest
+ *   step loads need K % 256 == 0 and a 16-byte aligned steps pointer. */
 int qlin_gemm_w4a16(const qlin_bf16* a, int64_t lda, const uint8_t* codes,
                     const qlin_bf16* steps, int64_t M, int64_t N, int64_t K, void* y,
                     int out_dtype, void* ws, size_t ws_bytes, qlin_stream_t stream);
