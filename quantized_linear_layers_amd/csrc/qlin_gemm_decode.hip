@@ -231,9 +231,12 @@ static int decode_cus() {
 // K=5120, N=25600: 22.7 instead of 23.6 us at M = 1; W4A16 from MB = 3,
 // where it halves the activation fragments read per weight byte; at M <= 16
 // it was slower). Split-K costs a write and a read of S*M*N partial
-// sums, so it is used only to reach that many workgroups (W4A16 with one
-// block above 16 rows, bound by its unpack and MFMA issue rather than by
-// HBM, wants two per CU); each split keeps >= 4 steps of 128 K.
+// sums and a second, serial phase, so fp8/int8 split only when the column
+// tiles reach fewer than half the CUs (K=2048, N=8192, 128 tiles: M = 1
+// 5.5 us unsplit, 6.2 us in 2 splits); W4A16, bound by its unpack and MFMA
+// issue rather than by HBM, splits to about three quarters of the CUs, and
+// with one block above 16 rows to two workgroups per CU. Each split keeps
+// >= 4 steps of 128 K.
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   const int64_t cus = decode_cus();
@@ -243,7 +246,7 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   const int64_t cols = (int64_t)16 * c.NW * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
-  const int64_t want = kind == kGemmW4 && c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
+  const int64_t want = kind != kGemmW4 ? cus / 2 : c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
   int64_t S = (want + c.tiles - 1) / c.tiles;
   S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
   if (const char* e = getenv("QLIN_DECODE_SPLIT")) S = std::max(1, atoi(e));  // tuning override
