@@ -53,15 +53,21 @@ struct GemmArgs {
 };
 
 // Decode-shaped GEMM: the streaming core of qlin_skinny.h over this
-// workgroup's 64*NB columns and this split's K range, then the split-K
-// reduction and the epilogue.
-template <int KIND, int MB, int NB, int DEPTH, bool SB, int NW>
+// workgroup's 16*NB*NW columns and this split's K range, then the split-K
+// reduction and the epilogue. With WK the NW waves share 16*NB columns and
+// each takes a quarter of the split's K range (whole 256-K chunks) with its
+// own activation chunks; their accumulators are summed through LDS in wave
+// order (deterministic) and wave 0 goes on alone. This puts a small layer's
+// whole weight matrix in flight at once without a second, global pass.
+template <int KIND, int MB, int NB, int DEPTH, bool SB, int NW, bool WK>
 __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) {
   using Acc = SkinnyAcc<KIND>;
   constexpr bool W4 = KIND == kGemmW4;
   constexpr int ESZ = W4 ? 2 : 1;
-  constexpr int kPer = skinny_pieces<KIND, MB, NW>();
-  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<KIND, MB, NB, DEPTH, NW>()];
+  constexpr int kPer = skinny_pieces<KIND, MB, NW, WK>();
+  constexpr int kLds = skinny_lds_bytes<KIND, MB, NB, DEPTH, NW, WK>();
+  static_assert(!WK || kLds >= NW * MB * NB * 64 * 16, "LDS holds the waves' accumulators");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   __shared__ unsigned last_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -69,7 +75,11 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
   const int r = lane & 15, g = lane >> 4;
   const int split = blockIdx.y, S = gridDim.y;
   const int k0 = split * p.kc, k1 = min(k0 + p.kc, p.K);
-  const int n0 = (blockIdx.x * NW + wave) * 16 * NB;  // this wave's first column
+  const int n0 = WK ? blockIdx.x * 16 * NB : (blockIdx.x * NW + wave) * 16 * NB;  // this wave's first column
+  // this wave's K range
+  const int kq = WK ? (k1 - k0 + NW * 256 - 1) / (NW * 256) * 256 : 0;
+  const int wk0 = WK ? min(k0 + wave * kq, k1) : k0;
+  const int wk1 = WK ? min(wk0 + kq, k1) : k1;
 
   // operand rows (clamped onto valid rows; padding activation rows masked)
   const uint8_t* wp[NB][2];
@@ -87,7 +97,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
   uint32_t am[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) {
-    const int row = (tid + 64 * NW * q) / (16 * ESZ);
+    const int row = ((WK ? lane : tid) + (WK ? 64 : 64 * NW) * q) / (16 * ESZ);
     ap[q] = p.A + (size_t)min(row, p.M - 1) * p.lda * ESZ;
     am[q] = row < p.M ? 0xFFFFFFFFu : 0u;
   }
@@ -107,7 +117,28 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[mb][j] = Acc{0, 0, 0, 0};
-  skinny_mma<KIND, MB, NB, DEPTH, SB, NW>(lds, wp, sp, ap, am, p.K, k0, k1, acc);
+  if (wk0 < wk1) skinny_mma<KIND, MB, NB, DEPTH, SB, NW, WK>(lds, wp, sp, ap, am, p.K, wk0, wk1, acc);
+
+  // ---- WK: sum the waves' accumulators (wave order), wave 0 owns the tile
+  bool owner = true;
+  if constexpr (WK) {
+    __syncthreads();  // every wave is done with its LDS regions
+    Acc* red = reinterpret_cast<Acc*>(lds);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) red[((wave * MB + mb) * NB + j) * 64 + lane] = acc[mb][j];
+    __syncthreads();
+    owner = wave == 0;
+    if (owner) {
+#pragma unroll
+      for (int w = 1; w < NW; ++w)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) acc[mb][j] = acc[mb][j] + red[((w * MB + mb) * NB + j) * 64 + lane];
+    }
+  }
 
   // ---- split-K: publish partials, the last workgroup of the tile reduces
   float accf[MB][NB][4];
@@ -137,7 +168,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = mb * 16 + 4 * g + i, n = n0 + 16 * j + r;
-          if (m < p.M && n < p.N)
+          if (owner && m < p.M && n < p.N)
             __hip_atomic_store(&p.part[((size_t)split * p.M + m) * p.N + n],
                                KIND == kGemmI8 ? (uint32_t)acci[mb][j][i] : __float_as_uint(accf[mb][j][i]),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -148,7 +179,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
       last_flag = __hip_atomic_fetch_add(&p.cnt[blockIdx.x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                   (unsigned)(S - 1);
     __syncthreads();
-    if (!last_flag) return;
+    if (!last_flag || !owner) return;
     // sum the splits in split order; every load of one split is issued
     // before the first is consumed (clamped addresses, no branches)
     const size_t stride = (size_t)p.M * p.N;
@@ -186,6 +217,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
     }
     if (tid == 0) __hip_atomic_store(&p.cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (!owner) return;
 
   // ---- epilogue
 #pragma unroll
@@ -211,6 +243,7 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
 // ----------------------------------------------------------------------------
 struct DecodeCfg {
   int MB, NB, NW;
+  bool WK;
   int tiles, S, kc;
 };
 
@@ -243,7 +276,13 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   c.MB = (int)((M + 15) / 16);
   c.NB = (kind != kGemmW4 || c.MB >= 3) && (N + 127) / 128 >= 3 * cus / 4 ? 2 : 1;
   c.NW = kind == kGemmW4 && c.NB == 2 ? 8 : 4;
-  const int64_t cols = (int64_t)16 * c.NW * c.NB;
+  // W4A16 at M <= 16 on a layer too narrow for the column tiles to fill the
+  // device: the 4 waves of a workgroup split K instead of the grid (one
+  // block each; K=2048, N=8192, M = 1: 5.9 instead of 6.9 us with 2 global
+  // splits; for fp8/int8 and on wide layers it was slower)
+  c.WK = kind == kGemmW4 && c.MB == 1 && (N + 63) / 64 < 3 * cus / 4;
+  if (c.WK) c.NB = 1;
+  const int64_t cols = (int64_t)16 * (c.WK ? 1 : c.NW) * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
   const int64_t want = kind != kGemmW4 ? cus / 2 : c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
@@ -266,17 +305,18 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
 // waits; K=5120, N=25600, M=64: 43.7 instead of 52.4 us; with one block
 // per wave, or fp8/int8, 8 waves measured no better).
 template <typename F>
-static auto with_decode_inst(int kind, int MB, int NB, bool sb, F&& f) {
+static auto with_decode_inst(int kind, int MB, int NB, bool wk, bool sb, F&& f) {
 #define QLIN_DEC(K, D1, D2, D22, NW2, SB)                                                          \
   switch (MB) {                                                                              \
     case 1:                                                                                  \
-      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 1, 2, D2, SB, 4>(); \
-      return f.template operator()<K, 1, 1, D1, SB, 4>();                                    \
+      if constexpr (K == kGemmW4) if (wk) return f.template operator()<K, 1, 1, D1, SB, 4, true>(); \
+      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 1, 2, D2, SB, 4, false>(); \
+      return f.template operator()<K, 1, 1, D1, SB, 4, false>();                             \
     case 2:                                                                                  \
-      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 2, 2, D2, SB, 4>(); \
-      return f.template operator()<K, 2, 1, D2, SB, 4>();                                    \
-    case 3: return NB == 2 ? f.template operator()<K, 3, 2, D22, SB, NW2>() : f.template operator()<K, 3, 1, D2, SB, 4>(); \
-    default: return NB == 2 ? f.template operator()<K, 4, 2, D22, SB, NW2>() : f.template operator()<K, 4, 1, D2, SB, 4>(); \
+      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 2, 2, D2, SB, 4, false>(); \
+      return f.template operator()<K, 2, 1, D2, SB, 4, false>();                             \
+    case 3: return NB == 2 ? f.template operator()<K, 3, 2, D22, SB, NW2, false>() : f.template operator()<K, 3, 1, D2, SB, 4, false>(); \
+    default: return NB == 2 ? f.template operator()<K, 4, 2, D22, SB, NW2, false>() : f.template operator()<K, 4, 1, D2, SB, 4, false>(); \
   }
   if (kind == kGemmW4) {
     if (sb) {
@@ -308,9 +348,9 @@ struct LaunchFn {
   const GemmArgs* a;
   const DecodeCfg* c;
   hipStream_t st;
-  template <int KIND, int MB, int NB, int DEPTH, bool SB, int NW>
+  template <int KIND, int MB, int NB, int DEPTH, bool SB, int NW, bool WK>
   int operator()() const {
-    decode_gemm_kernel<KIND, MB, NB, DEPTH, SB, NW><<<dim3((unsigned)c->tiles, (unsigned)c->S), 64 * NW, 0, st>>>(*a);
+    decode_gemm_kernel<KIND, MB, NB, DEPTH, SB, NW, WK><<<dim3((unsigned)c->tiles, (unsigned)c->S), 64 * NW, 0, st>>>(*a);
     return 0;
   }
 };
@@ -339,7 +379,7 @@ int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const v
   }
   // int4 steps in 16-byte pieces of 8 groups: aligned rows, whole pieces
   const bool sb = kind == kGemmW4 && K % 256 == 0 && ((uintptr_t)wsc & 15) == 0;
-  with_decode_inst(kind, c.MB, c.NB, sb, LaunchFn{&g, &c, st});
+  with_decode_inst(kind, c.MB, c.NB, c.WK, sb, LaunchFn{&g, &c, st});
   return launch_status();
 }
 

@@ -49,16 +49,19 @@ namespace qlin {
 template <int KIND>
 using SkinnyAcc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
 
-// Per-workgroup LDS bytes of skinny_mma<KIND, MB, NB, DEPTH, SB, NW>.
-template <int KIND, int MB, int NB, int DEPTH, int NW = 4>
+// Per-workgroup LDS bytes of skinny_mma<KIND, MB, NB, DEPTH, SB, NW, WK>.
+template <int KIND, int MB, int NB, int DEPTH, int NW = 4, bool WK = false>
 constexpr int skinny_lds_bytes() {
-  return 2 * MB * 2 * 16 * 128 * (KIND == kGemmW4 ? 2 : 1) + NW * NB * (2048 + (KIND == kGemmW4 ? 256 * DEPTH : 0));
+  return (WK ? NW : 1) * 2 * MB * 2 * 16 * 128 * (KIND == kGemmW4 ? 2 : 1) +
+         NW * NB * (2048 + (KIND == kGemmW4 ? 256 * DEPTH : 0));
 }
 
-// Activation pieces (16 bytes) each of the 64*NW threads stages per chunk.
-template <int KIND, int MB, int NW>
+// Activation pieces (16 bytes) each thread stages per chunk: the chunk is
+// split over the 64*NW threads of the workgroup, or with WK over the 64
+// lanes of each wave.
+template <int KIND, int MB, int NW, bool WK = false>
 constexpr int skinny_pieces() {
-  return MB * (KIND == kGemmW4 ? 2 : 1) * 4 / NW;
+  return MB * (KIND == kGemmW4 ? 2 : 1) * 4 / (WK ? 1 : NW);
 }
 
 // One weight unit of one wave in registers.
@@ -82,10 +85,14 @@ struct SkinnySlot<kGemmW4, NB> {
 //  am[q]     0xFFFFFFFF if that row is a real row, else 0 (the real rows
 //            must be a prefix of the tile's rows);
 //  K         full K (clamps the activation loads), k0/k1 the range.
-template <int KIND, int MB, int NB, int DEPTH, bool SB = false, int NW = 4>
+// WK: every wave has its own K range [k0, k1) (the arguments differ per
+// wave) and stages its own activation chunks in a wave-private LDS region
+// (no workgroup barriers inside; LDS operations of one wave complete in
+// order). The caller sums the waves' accumulators.
+template <int KIND, int MB, int NB, int DEPTH, bool SB = false, int NW = 4, bool WK = false>
 __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB][2], const uint16_t* (&sp)[NB],
-                                           const uint8_t* (&ap)[skinny_pieces<KIND, MB, NW>()],
-                                           uint32_t (&am)[skinny_pieces<KIND, MB, NW>()], int K, int k0,
+                                           const uint8_t* (&ap)[skinny_pieces<KIND, MB, NW, WK>()],
+                                           uint32_t (&am)[skinny_pieces<KIND, MB, NW, WK>()], int K, int k0,
                                            int k1, SkinnyAcc<KIND> (&acc)[MB][NB]) {
   constexpr bool W4 = KIND == kGemmW4;
   constexpr int ESZ = W4 ? 2 : 1;                    // activation bytes per element
@@ -95,19 +102,25 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   constexpr int kBlk = 16 * 128 * ESZ;               // LDS bytes per (mb, step) of activations
   constexpr int kBuf = MB * 2 * kBlk;                // one 256-K activation chunk
   constexpr int kRowPieces = 16 * ESZ;               // 16-byte pieces per row per chunk
-  constexpr int NT = 64 * NW;                        // threads of the workgroup
-  constexpr int kPer = skinny_pieces<KIND, MB, NW>();  // activation pieces per thread per chunk
-  static_assert(kPer * NW == MB * ESZ * 4 && kPer >= 1, "activation chunk split over the threads");
+  constexpr int NT = WK ? 64 : 64 * NW;              // threads staging one activation chunk
+  constexpr int kPer = skinny_pieces<KIND, MB, NW, WK>();  // activation pieces per thread per chunk
+  static_assert(kPer * NT == MB * ESZ * 256 && kPer >= 1, "activation chunk split over the threads");
   constexpr int kWSlot = NB * 2048;                  // one wave's weight unit in LDS
   constexpr int kSSlot = W4 ? DEPTH * NB * 256 : 0;  // ... and its int4 group steps
   static_assert(!SB || (W4 && DEPTH <= 4), "bulk steps: W4A16, one load covers <= 4 units");
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int tid = WK ? lane : (int)threadIdx.x;      // index among the staging threads
   const int r = lane & 15, g = lane >> 4;
   const int nunits = (k1 - k0 + kUnitK - 1) / kUnitK;
-  uint8_t* wslot = lds + 2 * kBuf + wave * kWSlot;
-  uint8_t* sslot = lds + 2 * kBuf + NW * kWSlot + wave * kSSlot;
+  constexpr int kActs = (WK ? NW : 1) * 2 * kBuf;    // activation region
+  uint8_t* const act = lds + (WK ? wave * 2 * kBuf : 0);
+  uint8_t* wslot = lds + kActs + wave * kWSlot;
+  uint8_t* sslot = lds + kActs + NW * kWSlot + wave * kSSlot;
+  auto block_sync = [&]() {
+    if constexpr (!WK) __syncthreads();
+  };
 
   // ---- weights
   const int wc = lane & 7;
@@ -182,7 +195,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
     int off;
     if constexpr (W4) off = (c & 3) * 1024 + (c >> 2) * 256 + ((rr ^ c) & 15) * 16;
     else off = (c >> 2) * 1024 + (c & 3) * 256 + ((rr ^ c) & 15) * 16;
-    return buf * kBuf + (mb * 2 + s) * kBlk + off;
+    return (int)(act - lds) + buf * kBuf + (mb * 2 + s) * kBlk + off;
   };
   auto aload = [&](int ci, uint4 (&dst)[kPer]) {
 #pragma unroll
@@ -213,7 +226,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   // multiply the weight unit in the wave's slot (unit u) with the
   // activation chunk that holds it
   auto compute = [&](int u, int d) {
-    const uint8_t* abase = lds + ((u / UPC) & 1) * kBuf;
+    const uint8_t* abase = act + ((u / UPC) & 1) * kBuf;
     if constexpr (W4) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -286,7 +299,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
     }
   }
   awrite(aset[0], 0, 0);
-  __syncthreads();
+  block_sync();
 
   // ---- main loop over whole rounds of DEPTH units. Activation chunk ci
   // uses LDS buffer ci & 1 and register set ci & 1; at its start the set is
@@ -314,7 +327,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
       compute(u, d);
       if (d % UPC == UPC - 1) {
         awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
-        __syncthreads();
+        block_sync();
       }
     }
   }
@@ -331,7 +344,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
       compute(u, d);
       if (d % UPC == UPC - 1 && d + 1 < rem) {
         awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
-        __syncthreads();
+        block_sync();
       }
     }
   }
