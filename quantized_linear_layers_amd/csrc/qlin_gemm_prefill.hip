@@ -13,7 +13,11 @@
 // Waves form a WM x WN grid; each wave owns (BM/WM) x (BN/WN) outputs as
 // 16x16 MFMA blocks. Tiles are ordered so that consecutive tiles of one XCD
 // share A rows (grouped order, XCD-major block remap).
+// Large FP8 / int8 problems use a persistent 256x256 kernel, one workgroup
+// per CU; when K is a multiple of 128 (and at least 256) its stages are
+// loaded straight into LDS by buffer loads, otherwise through registers.
 #include <algorithm>
+#include <type_traits>
 
 #include "qlin_device.h"
 #include "qlin_internal.h"
@@ -499,6 +503,255 @@ __global__ __launch_bounds__(256) void prefill_big_kernel(const PrefillArgs p, i
   }
 }
 
+// ----------------------------------------------------------------------------
+// The persistent 256x256 FP8 / int8 GEMM with direct-to-LDS staging (K a
+// multiple of 128, at least 256). Each stage's 64 KB arrive through
+// buffer_load_dwordx4 ... lds: the memory system writes every lane's 16 bytes
+// straight into LDS (lane i of an instruction at byte 16 i of a 1 KB block),
+// so staging takes no VGPRs and no LDS write instructions. LDS is row-major (128 bytes of K per row); chunk
+// c of row R sits in slot c ^ ((R >> 1) & 7), so one instruction (8 rows,
+// 8 lanes per row reading one whole 128-byte line) fills 1 KB contiguously
+// and a fragment read (16 lanes, one chunk of 16 consecutive rows) touches
+// every bank once.
+// Stage s is multiplied in 8 rows of 8 MFMAs. The stage barrier comes after
+// row 6: by then each wave has waited for its own loads of stage s + 1, and
+// every wave has read all of stage s it needs (row 7's blocks are in
+// registers). Row 7 then overlaps the reads of stage s + 1's fragments (each
+// W block register refilled right after its last MFMA) and the first loads
+// of stage s + 2 into the buffer stage s just released; the rest of those
+// loads follow during the first rows of stage s + 1.
+// The bf16 epilogue has an LDS area of its own and the scales two copies
+// (by tile parity), so loads stay in flight across it and it needs no
+// barrier.
+template <int KIND>
+__global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, int tiles_m,
+                                                          int tiles_n) {
+  constexpr int kStage = 65536, kWOff = 32768, kEpiRow = 272, kEpi = 16 * kEpiRow;
+  using Acc = typename std::conditional<KIND == kGemmI8, v4i, v4f>::type;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  __shared__ __attribute__((aligned(16))) float lds_sc[2][512];  // per tile parity: s_a rows, then s_w columns
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ep[4 * kEpi];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4, r = lane & 15;
+  const int KT = p.K >> 7;
+  const int tiles = tiles_m * tiles_n, G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+
+  // Load q (0..15) of this thread fills 1 KB block 4q + wave of A (q < 8) or
+  // W (q >= 8): tile row srow + 32q (or + 32(q-8)), chunk c of the stage.
+  const int srow = 8 * wave + (lane >> 3);
+  const int c = (lane & 7) ^ (4 * (wave & 1) + (lane >> 4));
+  const uint32_t kofs = 16u * (uint32_t)c;
+  const int rd0 = r * 128 + ((g ^ (r >> 1)) * 16);
+  const int rd1 = r * 128 + (((4 + g) ^ (r >> 1)) * 16);
+  const int ra = wm * 16384, rb = kWOff + wn * 16384;
+
+  v8i bf[8];  // W blocks of the current stage
+  Acc acc[8][8];
+
+  auto tile_origin = [&](int t, int& m0, int& n0) {
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (t / per_group) * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    m0 = (first_m + (t % per_group) % gsz) * 256;
+    n0 = ((t % per_group) / gsz) * 256;
+  };
+  // Loads are raw buffer loads (buffer_load_dwordx4 ... lds). The resource
+  // of a (matrix, tile, K stage) starts at the stage's first byte of the
+  // tile's first row and ends with the matrix, so rows past M (or N) are out
+  // of range: they read nothing (only outputs that are never stored depend
+  // on them). Each thread's 16 row offsets are fixed for the whole kernel;
+  // per stage only scalar registers change.
+  const uint32_t lda = (uint32_t)p.lda, ldw = (uint32_t)p.K;
+  uint32_t vo[16];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    vo[q] = (uint32_t)(32 * q + srow) * lda + kofs;
+    vo[8 + q] = (uint32_t)(32 * q + srow) * ldw + kofs;
+  }
+  auto rsrc = [&](const uint8_t* base, uint32_t ld, int rows_left, int kt) {
+    const uint64_t b = (uint64_t)(uintptr_t)(base + (size_t)kt * 128);
+    v4i r;
+    r.x = (int)(uint32_t)b;
+    r.y = (int)(uint32_t)(b >> 32);  // stride 0 (raw buffer)
+    r.z = (int)((uint32_t)rows_left * ld - (uint32_t)kt * 128u);
+    r.w = 0x00020000;  // gfx9 data format field (32-bit) as untyped loads need it
+    return r;
+  };
+  // Written as inline assembly: the compiler would otherwise treat every
+  // later LDS read as possibly aliasing the load and wait for all loads in
+  // flight before it. The kernel orders them itself (each wave waits for its
+  // own loads before the stage barrier, and before it exits).
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  auto dma = [&](int q, const v4i& rs, int buf) {
+    const uint32_t dst = lds_base + (uint32_t)(buf * kStage + 4096 * q + 1024 * wave);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(vo[q]), "s"(rs)
+                 : "memory", "m0");
+  };
+  // the resources of stage kt of the tile at (m0, n0): A, then W
+  auto stage_rs = [&](int m0, int n0, int kt, v4i& ra_, v4i& rw_) {
+    ra_ = rsrc(p.A + (size_t)m0 * lda, lda, p.M - m0, kt);
+    rw_ = rsrc(p.W + (size_t)n0 * ldw, ldw, p.N - n0, kt);
+  };
+  auto frag = [&](int off) {
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + off + rd0);
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + off + rd1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto mma = [&](int i, int j, const v8i& a, const v8i& w) {
+    if constexpr (KIND == kGemmFP8) {
+      acc[i][j] = mfma_fp8(w, a, acc[i][j]);
+    } else {
+      acc[i][j] = mfma_i8(__builtin_shufflevector(w, w, 0, 1, 2, 3), __builtin_shufflevector(a, a, 0, 1, 2, 3), acc[i][j]);
+      acc[i][j] = mfma_i8(__builtin_shufflevector(w, w, 4, 5, 6, 7), __builtin_shufflevector(a, a, 4, 5, 6, 7), acc[i][j]);
+    }
+  };
+  // load d of a stage is issued after MFMA number d * kSpread, counted from
+  // row 7 of the stage before (the 16 loads occupy the address unit for about
+  // half a stage; spreading them wider leaves the last too little time)
+  constexpr int kSpread = 2;
+  constexpr int kEarly = (8 + kSpread - 1) / kSpread;  // loads issued in row 7
+
+  if (slot >= tiles) return;
+  {
+    int m0, n0;
+    tile_origin(slot, m0, n0);
+    v4i r0, r1;
+    stage_rs(m0, n0, 0, r0, r1);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dma(q, q < 8 ? r0 : r1, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    stage_rs(m0, n0, 1, r0, r1);
+#pragma unroll
+    for (int q = 0; q < kEarly; ++q) dma(q, q < 8 ? r0 : r1, 1);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+  v8i af = frag(ra);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bf[j] = frag(rb + 2048 * j);
+
+  // One stage, multiplied from LDS buffer cb. (lm1, ln1, k1): tile origin
+  // and K stage of the next stage, whose loads this stage completes into
+  // buffer cb ^ 1; (lm2, ln2, k2): the stage after it, whose first loads
+  // row 7 issues into buffer cb.
+  auto stage = [&](int cb, int m0, int n0, int tp, int lm1, int ln1, int k1, int lm2, int ln2, int k2) {
+    const int cur = cb * kStage, nxt = (cb ^ 1) * kStage;
+    v4i a1, w1, a2, w2;
+    stage_rs(lm1, ln1, k1, a1, w1);
+    stage_rs(lm2, ln2, k2, a2, w2);
+    const float sc_a = p.sa[min(m0 + tid, p.M - 1)];
+    const float sc_w = p.sw[min(n0 + tid, p.N - 1)];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      const v8i an = frag(cur + ra + 2048 * (i + 1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        mma(i, j, af, bf[j]);
+        const int sl = 8 + 8 * i + j;
+        if (sl % kSpread == 0 && sl / kSpread < 16) dma(sl / kSpread, sl / kSpread < 8 ? a1 : w1, cb ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      af = an;
+    }
+    lds_sc[tp][tid] = sc_a;
+    lds_sc[tp][256 + tid] = sc_w;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const v8i an = frag(nxt + ra);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mma(7, j, af, bf[j]);
+      bf[j] = frag(nxt + rb + 2048 * j);
+      if (j % kSpread == 0 && j / kSpread < 16) dma(j / kSpread, j / kSpread < 8 ? a2 : w2, cb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    af = an;
+  };
+
+  int tp = 0, cb = 0;
+  for (int t = slot; t < tiles; t += G, tp ^= 1) {
+    int m0, n0, nm0, nn0;
+    tile_origin(t, m0, n0);
+    // the stages loaded ahead past this tile's last belong to the next tile
+    // of the workgroup; past the last tile they reload this tile's last stage
+    const bool nlive = t + G < tiles;
+    tile_origin(nlive ? t + G : t, nm0, nn0);
+    for (int kt = 0; kt < KT; ++kt, cb ^= 1) {
+      const bool in1 = kt + 1 < KT, in2 = kt + 2 < KT;
+      const int m1 = in1 ? m0 : nm0, n1 = in1 ? n0 : nn0, k1 = in1 ? kt + 1 : (nlive ? 0 : KT - 1);
+      const int m2 = in2 ? m0 : nm0, n2 = in2 ? n0 : nn0, k2 = in2 ? kt + 2 : (nlive ? kt + 2 - KT : KT - 1);
+      stage(cb, m0, n0, tp, m1, n1, k1, m2, n2, k2);
+    }
+
+    // ---- epilogue (see the kernel above for the lane layout)
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int eg = el >> 4, er = el & 15;
+    auto scaled = [&](int i, int j, int e) {
+      const float sa_i = lds_sc[tp][wm * 128 + i * 16 + er];
+      const float sw_e = lds_sc[tp][256 + wn * 128 + j * 16 + 4 * eg + e];
+      if constexpr (KIND == kGemmI8) return ((float)acc[i][j][e] * sa_i) * sw_e;
+      else return (acc[i][j][e] * sa_i) * sw_e;
+    };
+    if (p.out_f32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = m0 + wm * 128 + i * 16 + er;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int n = n0 + wn * 128 + j * 16 + 4 * eg;
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + (size_t)m * p.N + n) =
+                make_float4(scaled(i, j, 0), scaled(i, j, 1), scaled(i, j, 2), scaled(i, j, 3));
+        }
+      }
+    } else {
+      // bf16: transpose one 16-row block at a time through the wave's own
+      // LDS area (rows padded to 272 bytes), storing whole 256-byte row
+      // segments; the wave's LDS operations complete in order
+      uint8_t* ep = lds_ep + wave * kEpi;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t lo = f32_bf16_rne(scaled(i, j, 0)) | (f32_bf16_rne(scaled(i, j, 1)) << 16);
+          const uint32_t hi = f32_bf16_rne(scaled(i, j, 2)) | (f32_bf16_rne(scaled(i, j, 3)) << 16);
+          *reinterpret_cast<uint2*>(ep + er * kEpiRow + j * 32 + eg * 8) = make_uint2(lo, hi);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int R = 4 * k + eg, ch = er;
+          const uint4 v = *reinterpret_cast<const uint4*>(ep + R * kEpiRow + ch * 16);
+          const int m = m0 + wm * 128 + i * 16 + R;
+          const int n = n0 + wn * 128 + 8 * ch;
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.N + n) = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+    // the next stage's blocks (read by the last row 7) are read again here
+    // rather than kept live across the epilogue
+    af = frag(cb * kStage + ra);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bf[j] = frag(cb * kStage + rb + 2048 * j);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int KIND, int BM, int BN, int WM, int WN>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -520,6 +773,10 @@ template <int KIND>
 static void launch_prefill_big(const PrefillArgs& a, hipStream_t st) {
   const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
   const int grid = std::min(tm * tn, device_cus());
+  if (a.K % 128 == 0 && a.K >= 256) {
+    prefill_dma_kernel<KIND><<<dim3((unsigned)grid), 256, 0, st>>>(a, tm, tn);
+    return;
+  }
   if (a.K % 128 == 0) prefill_big_kernel<KIND, false><<<dim3((unsigned)grid), 256, 0, st>>>(a, tm, tn);
   else prefill_big_kernel<KIND, true><<<dim3((unsigned)grid), 256, 0, st>>>(a, tm, tn);
 }

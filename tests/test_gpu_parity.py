@@ -221,6 +221,8 @@ GEMM_CASES = [
     ("prefill_small", 1, 160, 416, (65, 130, 200)),
     # enough 256x256 tiles for the persistent kernel, with ragged M, N and K tails
     ("prefill_big_ragged", 1, 4112, 416, (2000,)),
+    # the same with K a multiple of 128 (the persistent kernel without K tail)
+    ("prefill_big_k384", 1, 4112, 384, (2000,)),
 ]
 
 
