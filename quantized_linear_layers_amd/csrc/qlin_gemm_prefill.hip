@@ -626,6 +626,7 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
     for (int q = 0; q < 16; ++q) dma(q, q < 8 ? r0 : r1, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // the first loads of the first step (stage 1), as a row 7 would issue them
     stage_rs(m0, n0, 1, r0, r1);
 #pragma unroll
     for (int q = 0; q < kEarly; ++q) dma(q, q < 8 ? r0 : r1, 1);
@@ -638,47 +639,65 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
 #pragma unroll
   for (int j = 0; j < 8; ++j) bf[j] = frag(rb + 2048 * j);
 
-  // One stage, multiplied from LDS buffer cb. (lm1, ln1, k1): tile origin
-  // and K stage of the next stage, whose loads this stage completes into
-  // buffer cb ^ 1; (lm2, ln2, k2): the stage after it, whose first loads
-  // row 7 issues into buffer cb.
-  auto stage = [&](int cb, int m0, int n0, int tp, int lm1, int ln1, int k1, int lm2, int ln2, int k2) {
-    const int cur = cb * kStage, nxt = (cb ^ 1) * kStage;
-    v4i a1, w1, a2, w2;
-    stage_rs(lm1, ln1, k1, a1, w1);
-    stage_rs(lm2, ln2, k2, a2, w2);
+  // The stream of (tile, K stage) pairs is cut after each stage barrier:
+  // one step is row 7 of stage s - 1 followed by rows 0..6 of stage s, so
+  // nothing is pending on the LDS counter where a step begins. All loads of
+  // one step go to stage s + 1 (for s + 1 = KT: stage 0 of the workgroup's
+  // next tile). A stage's data sits in LDS buffer (position in the stream)
+  // & 1.
+  //
+  // Row 7 of the stage before the one in buffer nb: its MFMAs, the refill of
+  // the W block registers and row 0's A block from buffer nb, and the first
+  // loads of the step (resources ra_/rw_) into buffer nb ^ 1.
+  auto row7 = [&](int nb, const v4i& ra_, const v4i& rw_) {
+    const v8i an = frag(nb * kStage + ra);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      mma(7, j, af, bf[j]);
+      bf[j] = frag(nb * kStage + rb + 2048 * j);
+      if (j % kSpread == 0) dma(j / kSpread, j / kSpread < 8 ? ra_ : rw_, nb ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    af = an;
+  };
+  // Rows 0..6 of the stage in buffer cb (tile at m0, n0; scale copy tp), the
+  // remaining loads of the step into buffer cb ^ 1, then the stage barrier.
+  // After row 3 (when the step's loads are all issued) `next` computes the
+  // next step's resources.
+  auto rows06 = [&](int cb, int m0, int n0, int tp, const v4i& ra_, const v4i& rw_, auto&& next) {
     const float sc_a = p.sa[min(m0 + tid, p.M - 1)];
     const float sc_w = p.sw[min(n0 + tid, p.N - 1)];
 #pragma unroll
     for (int i = 0; i < 7; ++i) {
-      const v8i an = frag(cur + ra + 2048 * (i + 1));
+      const v8i an = frag(cb * kStage + ra + 2048 * (i + 1));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         mma(i, j, af, bf[j]);
         const int sl = 8 + 8 * i + j;
-        if (sl % kSpread == 0 && sl / kSpread < 16) dma(sl / kSpread, sl / kSpread < 8 ? a1 : w1, cb ^ 1);
+        if (sl % kSpread == 0 && sl / kSpread < 16) dma(sl / kSpread, sl / kSpread < 8 ? ra_ : rw_, cb ^ 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       af = an;
+      if (i == 3) {
+        next();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     lds_sc[tp][tid] = sc_a;
     lds_sc[tp][256 + tid] = sc_w;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const v8i an = frag(nxt + ra);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      mma(7, j, af, bf[j]);
-      bf[j] = frag(nxt + rb + 2048 * j);
-      if (j % kSpread == 0 && j / kSpread < 16) dma(j / kSpread, j / kSpread < 8 ? a2 : w2, cb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    af = an;
   };
 
   int tp = 0, cb = 0;
+  v4i sa_rs, sw_rs;  // resources of the current step's loads
+  {
+    int m0, n0;
+    tile_origin(slot, m0, n0);
+    stage_rs(m0, n0, 1, sa_rs, sw_rs);
+  }
   for (int t = slot; t < tiles; t += G, tp ^= 1) {
     int m0, n0, nm0, nn0;
     tile_origin(t, m0, n0);
@@ -686,12 +705,25 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
     // of the workgroup; past the last tile they reload this tile's last stage
     const bool nlive = t + G < tiles;
     tile_origin(nlive ? t + G : t, nm0, nn0);
-    for (int kt = 0; kt < KT; ++kt, cb ^= 1) {
-      const bool in1 = kt + 1 < KT, in2 = kt + 2 < KT;
-      const int m1 = in1 ? m0 : nm0, n1 = in1 ? n0 : nn0, k1 = in1 ? kt + 1 : (nlive ? 0 : KT - 1);
-      const int m2 = in2 ? m0 : nm0, n2 = in2 ? n0 : nn0, k2 = in2 ? kt + 2 : (nlive ? kt + 2 - KT : KT - 1);
-      stage(cb, m0, n0, tp, m1, n1, k1, m2, n2, k2);
+    // resources of the loads for stage kt (kt >= KT: the next tile's)
+    v4i na_rs, nw_rs;
+    auto next_rs = [&](int kt) {
+      const bool in = kt < KT;
+      stage_rs(in ? m0 : nm0, in ? n0 : nn0, in ? kt : (nlive ? kt - KT : KT - 1), na_rs, nw_rs);
+    };
+    rows06(cb, m0, n0, tp, sa_rs, sw_rs, [&] { next_rs(2); });
+    sa_rs = na_rs;
+    sw_rs = nw_rs;
+    for (int kt = 1; kt < KT; ++kt) {
+      row7(cb ^ 1, sa_rs, sw_rs);
+      cb ^= 1;
+      rows06(cb, m0, n0, tp, sa_rs, sw_rs, [&] { next_rs(kt + 2); });
+      sa_rs = na_rs;
+      sw_rs = nw_rs;
     }
+    // the tile's last row 7; its loads are the next tile's stage 1
+    row7(cb ^ 1, sa_rs, sw_rs);
+    cb ^= 1;
 
     // ---- epilogue (see the kernel above for the lane layout)
     int el = lane;
