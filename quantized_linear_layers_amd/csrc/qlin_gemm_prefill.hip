@@ -593,9 +593,15 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
                  : "memory", "m0");
   };
   // the resources of stage kt of the tile at (m0, n0): A, then W
+  // Each XCD walks K from its own starting stage (k0, wrapping around), so
+  // the XCDs finish their tiles at different times and the bursts of output
+  // stores spread out; the workgroups of one XCD stay in step and keep
+  // sharing their A and W slices in L2.
+  const int k0 = (int)(((uint32_t)blockIdx.x % 8u) * (uint32_t)KT / 8u);
   auto stage_rs = [&](int m0, int n0, int kt, v4i& ra_, v4i& rw_) {
-    ra_ = rsrc(p.A + (size_t)m0 * lda, lda, p.M - m0, kt);
-    rw_ = rsrc(p.W + (size_t)n0 * ldw, ldw, p.N - n0, kt);
+    const int kp = kt + k0 < KT ? kt + k0 : kt + k0 - KT;
+    ra_ = rsrc(p.A + (size_t)m0 * lda, lda, p.M - m0, kp);
+    rw_ = rsrc(p.W + (size_t)n0 * ldw, ldw, p.N - n0, kp);
   };
   auto frag = [&](int off) {
     const v4i lo = *reinterpret_cast<const v4i*>(lds + off + rd0);
@@ -756,8 +762,8 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
       for (int i = 0; i < 8; ++i) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint32_t lo = f32_bf16_rne(scaled(i, j, 0)) | (f32_bf16_rne(scaled(i, j, 1)) << 16);
-          const uint32_t hi = f32_bf16_rne(scaled(i, j, 2)) | (f32_bf16_rne(scaled(i, j, 3)) << 16);
+          const uint32_t lo = pack_bf16x2(scaled(i, j, 0), scaled(i, j, 1));
+          const uint32_t hi = pack_bf16x2(scaled(i, j, 2), scaled(i, j, 3));
           *reinterpret_cast<uint2*>(ep + er * kEpiRow + j * 32 + eg * 8) = make_uint2(lo, hi);
         }
 #pragma unroll
@@ -766,8 +772,10 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
           const uint4 v = *reinterpret_cast<const uint4*>(ep + R * kEpiRow + ch * 16);
           const int m = m0 + wm * 128 + i * 16 + R;
           const int n = n0 + wn * 128 + 8 * ch;
+          // (nontemporal: the output is not read again here)
           if (m < p.M && n < p.N)
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.N + n) = v;
+            __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(&v),
+                                        reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.N + n));
         }
       }
     }
