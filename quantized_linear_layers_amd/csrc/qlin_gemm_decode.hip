@@ -180,8 +180,9 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
                   (unsigned)(S - 1);
     __syncthreads();
     if (!last_flag || !owner) return;
-    // sum the splits in split order; every load of one split is issued
-    // before the first is consumed (clamped addresses, no branches)
+    // sum the splits in split order; the loads of up to 4 splits are all
+    // issued before the first is consumed (each load is a round trip to
+    // memory; clamped addresses, no branches before the sums)
     const size_t stride = (size_t)p.M * p.N;
     uint32_t off[MB][NB][4];
 #pragma unroll
@@ -192,28 +193,37 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
         for (int i = 0; i < 4; ++i)
           off[mb][j][i] = (uint32_t)((size_t)min(mb * 16 + 4 * g + i, p.M - 1) * p.N +
                                      min(n0 + 16 * j + r, p.N - 1));
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      uint32_t u[4][MB][NB][4];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t* q = p.part + (size_t)min(s0 + b, S - 1) * stride;
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t u = __hip_atomic_load(&p.part[off[mb][j][i]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if constexpr (KIND == kGemmI8) acci[mb][j][i] = (int)u;
-          else accf[mb][j][i] = __uint_as_float(u);
-        }
-    for (int s = 1; s < S; ++s) {
-      uint32_t* q = p.part + (size_t)s * stride;
+          for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+            for (int i = 0; i < 4; ++i)
+              u[b][mb][j][i] = __hip_atomic_load(&q[off[mb][j][i]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+      for (int b = 0; b < 4; ++b) {
+        if (s0 + b >= S) break;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t u = __hip_atomic_load(&q[off[mb][j][i]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if constexpr (KIND == kGemmI8) acci[mb][j][i] += (int)u;
-            else accf[mb][j][i] = accf[mb][j][i] + __uint_as_float(u);
-          }
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (s0 + b == 0) {
+                if constexpr (KIND == kGemmI8) acci[mb][j][i] = (int)u[b][mb][j][i];
+                else accf[mb][j][i] = __uint_as_float(u[b][mb][j][i]);
+              } else {
+                if constexpr (KIND == kGemmI8) acci[mb][j][i] += (int)u[b][mb][j][i];
+                else accf[mb][j][i] = accf[mb][j][i] + __uint_as_float(u[b][mb][j][i]);
+              }
+            }
+      }
     }
     if (tid == 0) __hip_atomic_store(&p.cnt[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
