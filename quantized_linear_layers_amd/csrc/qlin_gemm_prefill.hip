@@ -792,6 +792,326 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// ----------------------------------------------------------------------------
+// Large W4A16 problems (K a multiple of 64, at least 128): the persistent
+// 256x256 kernel of the FP8 path with bf16 MFMAs (16x16x32) and the weights
+// unpacked in registers. A K stage is 64 elements: 256 rows of bf16 A (32 KB,
+// laid out and loaded as the FP8 kernel's stage), the int4 codes of 256
+// columns (8 KB, 32 bytes per column) and their group steps (1 KB, two per
+// column), all loaded straight into LDS by buffer loads.
+// K order inside a stage: MFMA lane group g of K step s takes the stage's
+// elements 16g + 8s .. 16g + 8s + 7, for A and W alike, so a lane's codes
+// for both K steps are 8 consecutive bytes of its column (one LDS read, one
+// group step) and its A piece for step s is the 16-byte chunk 2g + s of the
+// row. In LDS the two 16-byte halves of a column's codes swap places when
+// bit 3 of the column is set, which spreads the 8-byte code reads over all
+// banks.
+// Each wave owns 64 columns of the tile and all 256 rows, so every weight
+// is unpacked once per tile (the unpack, 17 VALU operations per 8 weights,
+// is this kernel's second largest cost after the MFMAs). The 32 A pieces of
+// a stage stay in registers; the wave walks its 4 column blocks, K step 0 of
+// the 16 row blocks then K step 1 (no MFMA waits for the one before it), and
+// spreads the unpack of the next column block over the current block's
+// MFMAs. The stage barrier comes after column block 2; column block 3
+// overlaps the refill of the A pieces and the unpack of the next stage's
+// first block with its MFMAs (as row 7 does in the FP8 kernel).
+__global__ __launch_bounds__(256) void prefill_w4_kernel(const PrefillArgs p, int tiles_m, int tiles_n) {
+  constexpr int kCOff = 32768, kSOff = 40960, kBuf = 41984;  // A | codes | steps
+  constexpr int kEpiRow = 144, kEpi = 16 * kEpiRow;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_ep[4 * kEpi];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int KT = p.K >> 6;
+  const int tiles = tiles_m * tiles_n, G = gridDim.x;
+  const int slot = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+
+  // A loads q = 0..7: 1 KB block 4q + wave (tile rows srow + 32q), chunk c
+  const int srow = 8 * wave + (lane >> 3);
+  const int c = (lane & 7) ^ (4 * (wave & 1) + (lane >> 4));
+  const uint32_t lda2 = (uint32_t)p.lda * 2u, kb2 = (uint32_t)p.K / 2u, ks2 = (uint32_t)p.K / 16u;
+  uint32_t vo[11];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) vo[q] = (uint32_t)(32 * q + srow) * lda2 + 16u * (uint32_t)c;
+  // code loads h = 0, 1: columns 32 (2 wave + h) + lane / 2, 16-byte half
+  // lane & 1 of the column's 32 bytes, swapped for columns with bit 3 set
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cc = 32 * (2 * wave + h) + (lane >> 1);
+    vo[8 + h] = (uint32_t)cc * kb2 + 16u * (uint32_t)((lane & 1) ^ ((cc >> 3) & 1));
+  }
+  vo[10] = (uint32_t)(64 * wave + lane) * ks2;  // step load: 4 bytes of column 64 wave + lane
+  // LDS read offsets: A piece of K step s (row r of a 16-row block), codes
+  // and step of column 64 wave + r (+ 16 per column block)
+  const int rdA0 = r * 128 + (((2 * g) ^ (r >> 1)) & 7) * 16;
+  const int rdA1 = r * 128 + (((2 * g + 1) ^ (r >> 1)) & 7) * 16;
+  const int rdC = kCOff + (64 * wave + r) * 32 + ((g ^ (((r >> 3) & 1) * 2)) * 8);
+  const int rdS = kSOff + (64 * wave + r) * 4 + (g >> 1) * 2;
+
+  v8bf af[16][2];  // A pieces of the current stage
+  v8bf bw[2][2];   // unpacked W: column block j in bw[j & 1]
+  v4f acc[16][4];
+
+  auto tile_origin = [&](int t, int& m0, int& n0) {
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int first_m = (t / per_group) * GM;
+    const int gsz = min(tiles_m - first_m, GM);
+    m0 = (first_m + (t % per_group) % gsz) * 256;
+    n0 = ((t % per_group) / gsz) * 256;
+  };
+  auto rsrc = [&](const uint8_t* base, uint64_t bytes_left) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    v4i rr;
+    rr.x = (int)(uint32_t)b;
+    rr.y = (int)(uint32_t)(b >> 32);
+    rr.z = (int)(uint32_t)bytes_left;
+    rr.w = 0x00020000;
+    return rr;
+  };
+  struct Rs {
+    v4i a, c, s;
+  };
+  const int k0 = (int)(((uint32_t)blockIdx.x % 8u) * (uint32_t)KT / 8u);
+  const uint8_t* steps8 = reinterpret_cast<const uint8_t*>(p.steps);
+  auto stage_rs = [&](int m0, int n0, int kt) {
+    const int kp = kt + k0 < KT ? kt + k0 : kt + k0 - KT;
+    Rs q;
+    q.a = rsrc(p.A + (size_t)m0 * lda2 + (size_t)kp * 128, (uint64_t)(p.M - m0) * lda2 - (uint64_t)kp * 128);
+    q.c = rsrc(p.W + (size_t)n0 * kb2 + (size_t)kp * 32, (uint64_t)(p.N - n0) * kb2 - (uint64_t)kp * 32);
+    q.s = rsrc(steps8 + (size_t)n0 * ks2 + (size_t)kp * 4, (uint64_t)(p.N - n0) * ks2 - (uint64_t)kp * 4);
+    return q;
+  };
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  // load d (0..10) of a stage into buffer buf (inline assembly: see the FP8
+  // kernel)
+  auto dma = [&](int d, const Rs& q, int buf) {
+    if (d < 8) {
+      const uint32_t dst = lds_base + (uint32_t)(buf * kBuf + 4096 * d + 1024 * wave);
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(vo[d]), "s"(q.a)
+                   : "memory", "m0");
+    } else if (d < 10) {
+      const uint32_t dst = lds_base + (uint32_t)(buf * kBuf + kCOff + 1024 * (2 * wave + d - 8));
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(dst), "v"(vo[d]), "s"(q.c)
+                   : "memory", "m0");
+    } else {
+      const uint32_t dst = lds_base + (uint32_t)(buf * kBuf + kSOff + 256 * wave);
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(dst), "v"(vo[10]), "s"(q.s)
+                   : "memory", "m0");
+    }
+  };
+  auto apiece = [&](int off) { return *reinterpret_cast<const v8bf*>(lds + off); };
+  // The unpack of one column block, in pieces placed between MFMAs:
+  // piece 0 reads the codes and the step, 1 turns the step into the
+  // unpack constants, 2..9 unpack the two words.
+  struct Unpack {
+    uint2 w;
+    uint32_t sb;
+    Int4Step st;
+    uint32_t t, p0, p1, p2, p3;
+    float f[8];
+  };
+  auto unpack_piece = [&](int k, int bb, int j, Unpack& u, v8bf& out0, v8bf& out1) {
+    constexpr uint32_t kMagic = 0x64006400u;
+    switch (k) {
+      case 0:
+        u.w = *reinterpret_cast<const uint2*>(lds + bb * kBuf + rdC + 512 * j);
+        u.sb = *reinterpret_cast<const uint16_t*>(lds + bb * kBuf + rdS + 64 * j);
+        break;
+      case 1: u.st = int4_step(__uint_as_float(u.sb << 16)); break;
+      case 2: case 6: {
+        const uint32_t x = k == 2 ? u.w.x : u.w.y;
+        u.t = x >> 8;
+        u.p0 = and_or(x, 0x000F000Fu, kMagic);
+        u.p1 = and_or(x, 0x00F000F0u, kMagic);
+        break;
+      }
+      case 3: case 7:
+        u.p2 = and_or(u.t, 0x000F000Fu, kMagic);
+        u.p3 = and_or(u.t, 0x00F000F0u, kMagic);
+        u.f[0] = fma_mix_lo(u.p0, u.st.s, u.st.off);
+        u.f[4] = fma_mix_hi(u.p0, u.st.s, u.st.off);
+        break;
+      case 4: case 8:
+        u.f[1] = fma_mix_lo(u.p1, u.st.s16, u.st.off16);
+        u.f[5] = fma_mix_hi(u.p1, u.st.s16, u.st.off16);
+        u.f[2] = fma_mix_lo(u.p2, u.st.s, u.st.off);
+        u.f[6] = fma_mix_hi(u.p2, u.st.s, u.st.off);
+        break;
+      default: {  // 5, 9
+        u.f[3] = fma_mix_lo(u.p3, u.st.s16, u.st.off16);
+        u.f[7] = fma_mix_hi(u.p3, u.st.s16, u.st.off16);
+        v4i q = {(int)pack_bf16x2(u.f[0], u.f[1]), (int)pack_bf16x2(u.f[2], u.f[3]),
+                 (int)pack_bf16x2(u.f[4], u.f[5]), (int)pack_bf16x2(u.f[6], u.f[7])};
+        (k == 5 ? out0 : out1) = __builtin_bit_cast(v8bf, q);
+      }
+    }
+  };
+  auto mma = [&](int i, int j, int s) { acc[i][j] = mfma_bf16(bw[j & 1][s], af[i][s], acc[i][j]); };
+  // load d of a step is issued after MFMA number 4 d + 1 of the step (the
+  // step's first 32 MFMAs are column block 3 of the stage before)
+  constexpr int kEarly = 8;  // loads issued in column block 3
+
+  if (slot >= tiles) return;
+  {
+    int m0, n0;
+    tile_origin(slot, m0, n0);
+    const Rs q0 = stage_rs(m0, n0, 0);
+#pragma unroll
+    for (int d = 0; d < 11; ++d) dma(d, q0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const Rs q1 = stage_rs(m0, n0, 1);
+#pragma unroll
+    for (int d = 0; d < kEarly; ++d) dma(d, q1, 1);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    af[i][0] = apiece(2048 * i + rdA0);
+    af[i][1] = apiece(2048 * i + rdA1);
+  }
+  {
+    Unpack u;
+#pragma unroll
+    for (int k = 0; k < 10; ++k) unpack_piece(k, 0, 0, u, bw[0][0], bw[0][1]);
+  }
+
+  // Column block 3 of the stage before the one in buffer nb, with the
+  // refill of the A pieces and the unpack of column block 0 from buffer nb,
+  // and the first loads of the step (resources q) into buffer nb ^ 1.
+  auto col3 = [&](int nb, const Rs& q) {
+    Unpack u;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int i = t & 15, s = t >> 4;
+      mma(i, 3, s);
+      if (s == 1) {
+        af[i][0] = apiece(nb * kBuf + 2048 * i + rdA0);
+        af[i][1] = apiece(nb * kBuf + 2048 * i + rdA1);
+      }
+      if (t >= 2 && t < 12) unpack_piece(t - 2, nb, 0, u, bw[0][0], bw[0][1]);
+      if (t % 4 == 1) dma(t / 4, q, nb ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Column blocks 0..2 of the stage in buffer cb, the remaining loads of the
+  // step into buffer cb ^ 1, then the stage barrier; `next` computes the
+  // next step's resources once its loads are issued.
+  auto cols02 = [&](int cb, const Rs& q, auto&& next) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      Unpack u;
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        mma(t & 15, j, t >> 4);  // consecutive MFMAs on different accumulators
+        if (t >= 1 && t < 11) unpack_piece(t - 1, cb, j + 1, u, bw[(j + 1) & 1][0], bw[(j + 1) & 1][1]);
+        const int sl = 32 * (j + 1) + t;
+        if (sl % 4 == 1 && sl / 4 < 11) dma(sl / 4, q, cb ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j == 1) {
+        next();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  int cb = 0;
+  Rs cur_rs;
+  {
+    int m0, n0;
+    tile_origin(slot, m0, n0);
+    cur_rs = stage_rs(m0, n0, 1);
+  }
+  for (int t = slot; t < tiles; t += G) {
+    int m0, n0, nm0, nn0;
+    tile_origin(t, m0, n0);
+    const bool nlive = t + G < tiles;
+    tile_origin(nlive ? t + G : t, nm0, nn0);
+    Rs nrs;
+    auto next_rs = [&](int kt) {
+      const bool in = kt < KT;
+      nrs = stage_rs(in ? m0 : nm0, in ? n0 : nn0, in ? kt : (nlive ? kt - KT : KT - 1));
+    };
+    cols02(cb, cur_rs, [&] { next_rs(2); });
+    cur_rs = nrs;
+    for (int kt = 1; kt < KT; ++kt) {
+      col3(cb ^ 1, cur_rs);
+      cb ^= 1;
+      cols02(cb, cur_rs, [&] { next_rs(kt + 2); });
+      cur_rs = nrs;
+    }
+    col3(cb ^ 1, cur_rs);
+    cb ^= 1;
+
+    // ---- epilogue: lane (g, r) of block (i, j) holds row 16i + r, columns
+    // 16j + 4g .. 16j + 4g + 3 of the wave's 256 x 64 part
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int eg = el >> 4, er = el & 15;
+    if (p.out_f32) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + i * 16 + er;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + 64 * wave + j * 16 + 4 * eg;
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + (size_t)m * p.N + n) =
+                make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+      }
+    } else {
+      // bf16: transpose each 16-row block through the wave's LDS area (rows
+      // of 128 bytes padded to 144) and store whole 128-byte row segments
+      uint8_t* ep = lds_ep + wave * kEpi;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          const uint32_t hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+          *reinterpret_cast<uint2*>(ep + er * kEpiRow + j * 32 + eg * 8) = make_uint2(lo, hi);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int R = 8 * k + (el >> 3), ch = el & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(ep + R * kEpiRow + ch * 16);
+          const int m = m0 + i * 16 + R;
+          const int n = n0 + 64 * wave + 8 * ch;
+          if (m < p.M && n < p.N)
+            __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(&v),
+                                        reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(p.y) + (size_t)m * p.N + n));
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0, 0, 0, 0};
+    // the next stage's A pieces and first unpacked block (made by the last
+    // column block 3) are made again here rather than kept live across the
+    // epilogue; buffer cb is not written before the next barrier
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      af[i][0] = apiece(cb * kBuf + 2048 * i + rdA0);
+      af[i][1] = apiece(cb * kBuf + 2048 * i + rdA1);
+    }
+    Unpack u;
+#pragma unroll
+    for (int kk = 0; kk < 10; ++kk) unpack_piece(kk, cb, 0, u, bw[0][0], bw[0][1]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int KIND, int BM, int BN, int WM, int WN>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
@@ -848,7 +1168,12 @@ int launch_prefill(int kind, const void* a, int64_t lda, const float* sa, const 
     if (big) launch_prefill_big<kGemmI8>(g, st);
     else launch_prefill_t<kGemmI8, 128, 128, 2, 2>(g, st);
   } else {
-    launch_prefill_t<kGemmW4, 128, 128, 2, 2>(g, st);
+    const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
+    if (tm * tn >= device_cus() / 2 && K % 64 == 0 && K >= 128 && (uint64_t)M * (uint64_t)lda * 2 < (1ull << 31) &&
+        (uint64_t)N * (uint64_t)K / 2 < (1ull << 31))
+      prefill_w4_kernel<<<dim3((unsigned)std::min(tm * tn, device_cus())), 256, 0, st>>>(g, tm, tn);
+    else
+      launch_prefill_t<kGemmW4, 128, 128, 2, 2>(g, st);
   }
   return launch_status();
 }
