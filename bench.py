@@ -323,7 +323,6 @@ def c4_rows(q, torch, gen, iters):
         codes, steps, _ = q.repack_q4_0(w)
         wq8, ws8 = q.repack_fp8(codes, steps)
         wi8, wsi8 = q.repack_int8(codes, steps)
-        del w, codes, steps
         x = dev(d["a"], torch)
         aq8, sa8 = q.quant_act(x, "e4m3")
         aqi, sai = q.quant_act(x, "int8")
@@ -332,8 +331,13 @@ def c4_rows(q, torch, gen, iters):
         t_q = T.time(lambda i: q.quant_act(x, "e4m3", out=(aq8, sa8)), n_it, filler_ms=5)
         t_g8 = T.time(lambda i: q.gemm_fp8(aq8, sa8, wq8, ws8, out=y), n_it, filler_ms=5)
         t_gi = T.time(lambda i: q.gemm_w8a8(aqi, sai, wi8, wsi8, out=y), n_it, filler_ms=5)
+        # W4A16 at the prefill shape (bf16 activations, int4 weights unpacked
+        # in the kernel) and torch's bf16 matmul on the same bf16 weights
+        t_w4 = T.time(lambda i: q.gemm_w4a16(x, codes, steps, out=y), n_it, filler_ms=5)
+        t_bf = T.time(lambda i: torch.matmul(x, w.t(), out=y), n_it, filler_ms=5)
         tag = f"C4_K{K}_N{N}"
-        for name, t, peak in (("fp8_gemm", t_g8, "fp8"), ("int8_gemm", t_gi, "int8")):
+        for name, t, peak in (("fp8_gemm", t_g8, "fp8"), ("int8_gemm", t_gi, "int8"),
+                              ("w4a16_gemm", t_w4, "bf16"), ("bf16_torch", t_bf, "bf16")):
             tf = flops / (t["mean_us"] * 1e-6) / 1e12
             rows[f"{tag}_{name}"] = dict(us=round(t["mean_us"], 1), TFLOPs=round(tf, 1),
                                          frac_mfma=round(tf / MFMA_PEAK_TFLOPS[peak], 4))
@@ -342,7 +346,7 @@ def c4_rows(q, torch, gen, iters):
         rows[f"{tag}_fp8_linear_incl_quant"] = dict(us=round(tot, 1), quant_us=round(t_q["mean_us"], 1),
                                                     TFLOPs=round(tf, 1),
                                                     frac_mfma=round(tf / MFMA_PEAK_TFLOPS["fp8"], 4))
-        del wq8, wi8, x, aq8, aqi, y
+        del wq8, wi8, x, aq8, aqi, y, w, codes, steps
         torch.cuda.empty_cache()
     return rows
 

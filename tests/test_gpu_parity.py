@@ -365,6 +365,22 @@ def test_gemm_c4_prefill_sampled(q, oracle, c4, fmt, which):
     assert np.array_equal(ylin, gen.to_bf16_bits(y))
 
 
+@pytest.mark.parametrize("which", [0, 1])
+def test_gemm_w4a16_c4_prefill_sampled(q, oracle, c4, which):
+    """W4A16 at the full prefill shape (M=8192, the persistent kernel):
+    sampled outputs against the oracle, and the bf16 output equal to the
+    fp32 output rounded to nearest even."""
+    d = c4[which]
+    a, pk, st = dev(d["a"]), dev(d["packed"]), dev(d["steps_bits"])
+    y = host(q.gemm_w4a16(a, pk, st, out_dtype=torch.float32))
+    y16 = host(q.gemm_w4a16(a, pk, st))
+    rng = np.random.default_rng(5 + which)
+    mi, ni = _sampled(rng, d["M"], d["N"], 2000)
+    ref = oracle.gemm_w4a16_sample(d["a"], d["packed"], d["steps_bits"], mi, ni)
+    tol_check(y[mi, ni], ref, f"w4a16 C4[{which}]", rms=float(np.sqrt(np.mean(ref.astype(np.float64) ** 2))))
+    assert np.array_equal(y16, gen.to_bf16_bits(y))
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
 def test_linear_decode(q, oracle, fmt):
     d = gen.linear_config(2, n=1024, m=8)
