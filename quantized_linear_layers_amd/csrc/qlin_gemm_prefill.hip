@@ -800,12 +800,13 @@ __global__ __launch_bounds__(256) void prefill_dma_kernel(const PrefillArgs p, i
 // columns (8 KB, 32 bytes per column) and their group steps (1 KB, two per
 // column), all loaded straight into LDS by buffer loads.
 // K order inside a stage: MFMA lane group g of K step s takes the stage's
-// elements 16g + 8s .. 16g + 8s + 7, for A and W alike, so a lane's codes
-// for both K steps are 8 consecutive bytes of its column (one LDS read, one
-// group step) and its A piece for step s is the 16-byte chunk 2g + s of the
-// row. In LDS the two 16-byte halves of a column's codes swap places when
-// bit 3 of the column is set, which spreads the 8-byte code reads over all
-// banks.
+// elements 32s + 8g .. 32s + 8g + 7 (group s of the stage), for A and W
+// alike: a lane's A piece for step s is the 16-byte chunk 4s + g of the row
+// (the FP8 kernel's fragment reads, conflict-free; the order 16g + 8s, which
+// would make a lane's codes one 8-byte read, measured 4 bank-conflict cycles
+// per A read) and its codes are dwords g and 4 + g of the column's 32 bytes.
+// In LDS the two 16-byte halves of a column's codes swap places when bit 3
+// of the column is set, which spreads the dword code reads over all banks.
 // Each wave owns 64 columns of the tile and all 256 rows, so every weight
 // is unpacked once per tile (the unpack, 17 VALU operations per 8 weights,
 // is this kernel's second largest cost after the MFMAs). The 32 A pieces of
@@ -845,10 +846,12 @@ __global__ __launch_bounds__(256) void prefill_w4_kernel(const PrefillArgs p, in
   vo[10] = (uint32_t)(64 * wave + lane) * ks2;  // step load: 4 bytes of column 64 wave + lane
   // LDS read offsets: A piece of K step s (row r of a 16-row block), codes
   // and step of column 64 wave + r (+ 16 per column block)
-  const int rdA0 = r * 128 + (((2 * g) ^ (r >> 1)) & 7) * 16;
-  const int rdA1 = r * 128 + (((2 * g + 1) ^ (r >> 1)) & 7) * 16;
-  const int rdC = kCOff + (64 * wave + r) * 32 + ((g ^ (((r >> 3) & 1) * 2)) * 8);
-  const int rdS = kSOff + (64 * wave + r) * 4 + (g >> 1) * 2;
+  const int rdA0 = r * 128 + ((g ^ (r >> 1)) & 7) * 16;
+  const int rdA1 = r * 128 + (((4 + g) ^ (r >> 1)) & 7) * 16;
+  const int sw4 = ((r >> 3) & 1) * 4;  // code dword d of the column sits at d ^ sw4
+  const int rdC0 = kCOff + (64 * wave + r) * 32 + 4 * (g ^ sw4);
+  const int rdC1 = kCOff + (64 * wave + r) * 32 + 4 * ((4 + g) ^ sw4);
+  const int rdS = kSOff + (64 * wave + r) * 4;
 
   v8bf af[16][2];  // A pieces of the current stage
   v8bf bw[2][2];   // unpacked W: column block j in bw[j & 1]
@@ -904,11 +907,10 @@ __global__ __launch_bounds__(256) void prefill_w4_kernel(const PrefillArgs p, in
   };
   auto apiece = [&](int off) { return *reinterpret_cast<const v8bf*>(lds + off); };
   // The unpack of one column block, in pieces placed between MFMAs:
-  // piece 0 reads the codes and the step, 1 turns the step into the
-  // unpack constants, 2..9 unpack the two words.
+  // piece 0 reads the two code words and the column's two steps, 1 and 6
+  // turn a step into the unpack constants, 2..5 and 6..9 unpack a word.
   struct Unpack {
-    uint2 w;
-    uint32_t sb;
+    uint32_t w0, w1, sb;
     Int4Step st;
     uint32_t t, p0, p1, p2, p3;
     float f[8];
@@ -917,12 +919,14 @@ __global__ __launch_bounds__(256) void prefill_w4_kernel(const PrefillArgs p, in
     constexpr uint32_t kMagic = 0x64006400u;
     switch (k) {
       case 0:
-        u.w = *reinterpret_cast<const uint2*>(lds + bb * kBuf + rdC + 512 * j);
-        u.sb = *reinterpret_cast<const uint16_t*>(lds + bb * kBuf + rdS + 64 * j);
+        u.w0 = *reinterpret_cast<const uint32_t*>(lds + bb * kBuf + rdC0 + 512 * j);
+        u.w1 = *reinterpret_cast<const uint32_t*>(lds + bb * kBuf + rdC1 + 512 * j);
+        u.sb = *reinterpret_cast<const uint32_t*>(lds + bb * kBuf + rdS + 64 * j);
         break;
       case 1: u.st = int4_step(__uint_as_float(u.sb << 16)); break;
       case 2: case 6: {
-        const uint32_t x = k == 2 ? u.w.x : u.w.y;
+        if (k == 6) u.st = int4_step(__uint_as_float(u.sb & 0xFFFF0000u));
+        const uint32_t x = k == 2 ? u.w0 : u.w1;
         u.t = x >> 8;
         u.p0 = and_or(x, 0x000F000Fu, kMagic);
         u.p1 = and_or(x, 0x00F000F0u, kMagic);
