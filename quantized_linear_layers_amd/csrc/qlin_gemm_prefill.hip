@@ -999,7 +999,7 @@ __global__ __launch_bounds__(256) void prefill_w4_kernel(const PrefillArgs p, in
         af[i][0] = apiece(nb * kBuf + 2048 * i + rdA0);
         af[i][1] = apiece(nb * kBuf + 2048 * i + rdA1);
       }
-      if (t >= 2 && t < 12) unpack_piece(t - 2, nb, 0, u, bw[0][0], bw[0][1]);
+      if (t % 3 == 2 && t / 3 < 10) unpack_piece(t / 3, nb, 0, u, bw[0][0], bw[0][1]);
       if (t % 4 == 1) dma(t / 4, q, nb ^ 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1014,7 +1014,8 @@ __global__ __launch_bounds__(256) void prefill_w4_kernel(const PrefillArgs p, in
 #pragma unroll
       for (int t = 0; t < 32; ++t) {
         mma(t & 15, j, t >> 4);  // consecutive MFMAs on different accumulators
-        if (t >= 1 && t < 11) unpack_piece(t - 1, cb, j + 1, u, bw[(j + 1) & 1][0], bw[(j + 1) & 1][1]);
+        // (one unpack piece after every third MFMA)
+        if (t % 3 == 1 && t / 3 < 10) unpack_piece(t / 3, cb, j + 1, u, bw[(j + 1) & 1][0], bw[(j + 1) & 1][1]);
         const int sl = 32 * (j + 1) + t;
         if (sl % 4 == 1 && sl / 4 < 11) dma(sl / 4, q, cb ^ 1);
         __builtin_amdgcn_sched_barrier(0);
