@@ -59,6 +59,7 @@ def _load():
         "qo_moe_gate_up": (None, [P, P, I64, I64, I64, C.c_int, P, P, P, P]),
         "qo_moe_down": (None, [P, P, I64, I64, I64, C.c_int, P, P, P, P, P, P, P]),
         "qo_moe_fp8": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "qo_moe_w4a16": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, P, P, P, P]),
         "qo_max_threads": (C.c_int, []),
     }
     for name, (res, args) in sig.items():
@@ -313,6 +314,27 @@ def moe_down(aq, sa, ids, probs, w2, s2):
     _load().qo_moe_down(_p(aq), _p(sa), T, H, I, topk, _p(ids), _p(probs), _p(w2), _p(s2),
                         _p(d32), _p(y32), _p(y16))
     return d32, y32, y16
+
+
+def moe_w4a16(x_bf16, ids, probs, p13, st13, p2, st2):
+    """Full W4A16 MoE block. p13 [E,2I,H/2] u8 codes, st13 [E,2I,H/32] bf16
+    steps, p2 [E,H,I/2], st2 [E,H,I/32].
+
+    Returns dict with act16 [T*topk,I] (bf16 bits), d32 [T*topk,H], y32 [T,H], y16.
+    """
+    x = _c(x_bf16, np.uint16)
+    ids, probs = _c(ids, np.int32), _c(probs, np.float32)
+    p13, st13, p2, st2 = _c(p13, np.uint8), _c(st13, np.uint16), _c(p2, np.uint8), _c(st2, np.uint16)
+    T, H = x.shape
+    E, I2, _ = p13.shape
+    I = I2 // 2
+    topk = ids.shape[1]
+    R = T * topk
+    out = dict(act16=np.empty((R, I), np.uint16), d32=np.empty((R, H), np.float32),
+               y32=np.empty((T, H), np.float32), y16=np.empty((T, H), np.uint16))
+    _load().qo_moe_w4a16(_p(x), T, H, I, E, topk, _p(ids), _p(probs), _p(p13), _p(st13), _p(p2),
+                         _p(st2), _p(out["act16"]), _p(out["d32"]), _p(out["y32"]), _p(out["y16"]))
+    return out
 
 
 def max_threads() -> int:

@@ -650,6 +650,69 @@ void qo_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, i
   free(sx);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Mixture-of-experts W4A16 block ([SIZES] "The 4-Bit Builds Stay Slow": the */
+/* 4-bit MoE runs a WNA16 expert path -- bf16 activations, group-32 int4     */
+/* expert weights unpacked to bf16 -- on the fused gate_up / down banks split */
+/* per expert as in "Step 1"). The steps of the fp8 block without activation  */
+/* quantisation; the down projection takes bf16 activations, so the SiLU*up  */
+/* product is rounded to bf16 once. Weights: p13 [E][2I][H/2] packed codes,  */
+/* st13 [E][2I][H/32] bf16 steps (rows 0..I-1 gate, I..2I-1 up); p2          */
+/* [E][H][I/2], st2 [E][H][I/32]. wd = bf16(c*step) as in the W4A16 GEMM.    */
+/* For token t and slot j with expert e = ids[t,j], probability p = probs:   */
+/*   h = x . W13d_e^T               (fp32, k ascending; [2I])                */
+/*   act = bf16(SiLU(h[:I]) * h[I:])                                         */
+/*   d = act . W2d_e^T              (fp32, [H])                              */
+/*   y[t] = bf16(sum_j p_j * d_j), slot order j = 0..topk-1.                  */
+/* Stage outputs (may be NULL): act16 [T*topk, I] bf16 bits, d32             */
+/* [T*topk, H], y32 [T, H]; row index t*topk + j.                            */
+/* ------------------------------------------------------------------------ */
+void qo_moe_w4a16(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                  const int32_t* ids, const float* probs, const uint8_t* p13, const uint16_t* st13,
+                  const uint8_t* p2, const uint16_t* st2, uint16_t* act16, float* d32, float* y32,
+                  uint16_t* y16) {
+  (void)E;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    float* wrow = (float*)malloc((size_t)(H > I ? H : I) * sizeof(float));
+    uint16_t* act = (uint16_t*)malloc((size_t)I * sizeof(uint16_t));
+    float* d = (float*)malloc((size_t)(topk * H) * sizeof(float));
+    for (int j = 0; j < topk; ++j) {
+      const int64_t r = t * topk + j, e = ids[r];
+      for (int64_t i = 0; i < I; ++i) {
+        float g = 0.0f, u = 0.0f;
+        const int64_t rg = e * 2 * I + i, ru = e * 2 * I + I + i;
+        for (int64_t k = 0; k < H; ++k)
+          wrow[k] = bf16_value(bf16_nearest(grid_value(p13 + rg * (H / 2), st13 + rg * (H / 32), k)));
+        for (int64_t k = 0; k < H; ++k) g = g + bf16_value(x[t * H + k]) * wrow[k];
+        for (int64_t k = 0; k < H; ++k)
+          wrow[k] = bf16_value(bf16_nearest(grid_value(p13 + ru * (H / 2), st13 + ru * (H / 32), k)));
+        for (int64_t k = 0; k < H; ++k) u = u + bf16_value(x[t * H + k]) * wrow[k];
+        const float silu = g / (1.0f + expf(-g));
+        act[i] = bf16_nearest(silu * u);
+        if (act16) act16[r * I + i] = act[i];
+      }
+      for (int64_t h = 0; h < H; ++h) {
+        const int64_t rd = e * H + h;
+        float acc = 0.0f;
+        for (int64_t i = 0; i < I; ++i)
+          acc = acc + bf16_value(act[i]) * bf16_value(bf16_nearest(grid_value(p2 + rd * (I / 2), st2 + rd * (I / 32), i)));
+        d[j * H + h] = acc;
+        if (d32) d32[r * H + h] = acc;
+      }
+    }
+    for (int64_t h = 0; h < H; ++h) {
+      float y = 0.0f;
+      for (int j = 0; j < topk; ++j) y = y + probs[t * topk + j] * d[j * H + h];
+      if (y32) y32[t * H + h] = y;
+      if (y16) y16[t * H + h] = bf16_nearest(y);
+    }
+    free(wrow);
+    free(act);
+    free(d);
+  }
+}
+
 int qo_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -7,6 +7,11 @@ weight scales for the fp8 MoE) reduces to per-expert FP8 linears. A
 brute-force fp64 numpy version at a tiny size checks each stage; the
 requantisation between the two GEMMs is checked bit-exact against a
 brute-force quantiser on the oracle's own intermediate.
+
+The W4A16 block (sizes article, "The 4-Bit Builds Stay Slow": the 4-bit MoE
+runs vLLM's WNA16 expert path) is pinned the same way on the generator's
+materialised bf16 banks, plus its reduction to the W4A16 GEMM oracle at one
+expert per token and its linearity in the routing probabilities.
 """
 
 import numpy as np
@@ -96,3 +101,67 @@ def test_moe_single_expert_is_dense_linear(oracle):
         e = d["ids"][tok, 0]
         y32, _ = oracle.gemm_fp8(out["aq"][tok:tok + 1], out["sa"][tok:tok + 1], d["w2"][e], d["s2"][e])
         assert np.array_equal(out["y32"][tok], y32[0])
+
+
+# ---------------------------------------------------------------- W4A16 block
+def _w4_block(oracle, E=4, H=64, I=32, T=5, topk=2, seed=31):
+    """Packed codes and bf16 steps of every expert, recovered from the
+    generator's bf16 expert banks by the (separately pinned) q4_0 repack."""
+    d = gen.moe_config(E=E, H=H, I=I, T=T, topk=topk, seed=seed)
+    p13 = np.empty((E, 2 * I, H // 2), np.uint8); st13 = np.empty((E, 2 * I, H // 32), np.uint16)
+    p2 = np.empty((E, H, I // 2), np.uint8); st2 = np.empty((E, H, I // 32), np.uint16)
+    for e in range(E):
+        p13[e], st13[e], amb = oracle.repack_q4_0(d["w13_bf16"][e]); assert amb == 0
+        p2[e], st2[e], amb = oracle.repack_q4_0(d["w2_bf16"][e]); assert amb == 0
+    d.update(p13=p13, st13=st13, p2=p2, st2=st2)
+    return d
+
+
+def test_moe_w4a16_stages_bruteforce(oracle):
+    """fp64 numpy on the generator's materialised bf16 banks (bf16(c*step)
+    bit for bit under the bf16-step recipe): gate rows first, SiLU(g)*u
+    rounded once to bf16, down, probability-weighted sum in slot order."""
+    d = _w4_block(oracle)
+    out = oracle.moe_w4a16(d["x"], d["ids"], d["probs"], d["p13"], d["st13"], d["p2"], d["st2"])
+    T, topk, I, H = d["T"], d["topk"], d["I"], d["H"]
+    x = gen.bf16_bits_to_f32(d["x"]).astype(np.float64)
+    w13 = gen.bf16_bits_to_f32(d["w13_bf16"]).astype(np.float64)
+    w2 = gen.bf16_bits_to_f32(d["w2_bf16"]).astype(np.float64)
+    act16 = gen.bf16_bits_to_f32(out["act16"]).astype(np.float64)
+    y = np.zeros((T, H))
+    for r in range(T * topk):
+        tok, e = r // topk, d["ids"].ravel()[r]
+        h = x[tok] @ w13[e].T
+        g, u = h[:I], h[I:]
+        act = g / (1.0 + np.exp(-g)) * u
+        # one bf16 rounding (half an ulp) plus fp32 summation error
+        assert np.all(np.abs(act16[r] - act) <= 2.0 ** -8 * np.abs(act) + 1e-5 * np.sqrt(np.mean(act ** 2)))
+        dr = act16[r] @ w2[e].T
+        assert _close(out["d32"][r], dr)
+        y[tok] += float(d["probs"].ravel()[r]) * dr
+    assert _close(out["y32"], y, rel=1e-4)
+    assert np.array_equal(out["y16"], oracle.bf16_nearest_array(out["y32"]))
+
+
+def test_moe_w4a16_single_expert_is_w4a16_linear(oracle):
+    """topk=1 with probability 1: each token's output equals the W4A16 GEMM
+    oracle on its bf16 intermediate through that expert's down bank."""
+    d = _w4_block(oracle, T=3, topk=1, seed=13)
+    probs = np.ones_like(d["probs"])
+    out = oracle.moe_w4a16(d["x"], d["ids"], probs, d["p13"], d["st13"], d["p2"], d["st2"])
+    for tok in range(3):
+        e = d["ids"][tok, 0]
+        y32, _ = oracle.gemm_w4a16(out["act16"][tok:tok + 1], d["p2"][e], d["st2"][e])
+        assert np.array_equal(out["y32"][tok], y32[0])
+
+
+def test_moe_w4a16_linear_in_probabilities(oracle):
+    """Doubling every routing probability doubles the fp32 output exactly;
+    zero probabilities give zero."""
+    d = _w4_block(oracle, seed=17)
+    a = oracle.moe_w4a16(d["x"], d["ids"], d["probs"], d["p13"], d["st13"], d["p2"], d["st2"])
+    b = oracle.moe_w4a16(d["x"], d["ids"], 2 * d["probs"], d["p13"], d["st13"], d["p2"], d["st2"])
+    z = oracle.moe_w4a16(d["x"], d["ids"], 0 * d["probs"], d["p13"], d["st13"], d["p2"], d["st2"])
+    assert np.array_equal(b["y32"], 2 * a["y32"])
+    assert np.array_equal(b["act16"], a["act16"])
+    assert not np.any(z["y32"])
