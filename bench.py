@@ -381,6 +381,30 @@ def c5_rows(q, torch, gen, iters):
                                          frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
     del copies, w13, w2
     torch.cuda.empty_cache()
+    # W4A16 block: packed codes and bf16 group steps of every expert, read
+    # in place by the grouped GEMMs
+    c13 = torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, device="cuda")
+    t13 = torch.empty(E, 2 * I, H // 32, dtype=torch.bfloat16, device="cuda")
+    c2 = torch.empty(E, H, I // 2, dtype=torch.uint8, device="cuda")
+    t2 = torch.empty(E, H, I // 32, dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        c13[e], t13[e], _ = q.repack_q4_0(dev(d["w13_bf16"][e], torch))
+        c2[e], t2[e], _ = q.repack_q4_0(dev(d["w2_bf16"][e], torch))
+    copies = [(c13, t13, c2, t2)] + [tuple(a.clone() for a in (c13, t13, c2, t2)) for _ in range(2)]
+    for Tn in (64, 512):
+        x = dev(d["x"][:Tn], torch)
+        ids = dev(d["ids"][:Tn], torch)
+        pr = dev(d["probs"][:Tn], torch)
+        touched = len(set(d["ids"][:Tn].ravel().tolist()))
+        wb = touched * (2 * I * H // 2 + 2 * I * (H // 32) * 2 + H * I // 2 + H * (I // 32) * 2)
+        t = T.time(lambda i: q.moe_w4a16(x, ids, pr, *copies[i % len(copies)]), max(6, iters // 4),
+                   filler_ms=5)
+        gbs = wb / (t["mean_us"] * 1e3)
+        rows[f"C5_moe_w4a16_T{Tn}"] = dict(us=round(t["mean_us"], 1), experts_touched=touched,
+                                           weight_bytes=wb, GBps=round(gbs, 1),
+                                           frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+    del copies, c13, c2
+    torch.cuda.empty_cache()
     return rows
 
 

@@ -255,6 +255,41 @@ size_t qlin_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int 
 int qlin_moe_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk,
                               size_t offsets[6]);
 
+/* ------------------------------------------------------------------------
+ * W4A16 mixture-of-experts block ([SIZES] "The 4-Bit Builds Stay Slow": the
+ * 4-bit builds of the MoE model run a WNA16 expert path -- bf16 activations,
+ * group-32 int4 expert weights -- on the expert banks split per expert as in
+ * "Step 1"). Routing is an input, as for qlin_moe_fp8.
+ *   x [T][H] bf16; topk_ids [T][topk] int32 in [0,E); topk_w [T][topk] fp32;
+ *   codes13 [E][2I][H/2] packed int4 (layout of qlin_repack_q4_0; rows
+ *   0..I-1 gate, I..2I-1 up), steps13 [E][2I][H/32] bf16;
+ *   codes2 [E][H][I/2], steps2 [E][H][I/32]; y [T][H] bf16.
+ * With wd = bf16(c * step), for token t and slot j (expert e, weight p):
+ *   h = x . W13d[e]^T (fp32);  g = h[:I], u = h[I:];
+ *   act = bf16(SiLU(g) * u)   (computed in fp32, rounded once);
+ *   d = act . W2d[e]^T        (fp32);
+ *   y[t] = bf16(sum_j p_j * d_j), summed in slot order j = 0..topk-1.
+ * Expert ids outside [0, E) contribute nothing. H, I multiples of 32; x,
+ * codes and y 16-byte aligned, steps 2-byte aligned (16-byte aligned step
+ * rows with H, I multiples of 256 take the faster bulk step loads).
+ * Workspace: qlin_moe_w4a16_workspace_bytes(T, H, I, E, topk) bytes,
+ * 256-byte aligned (no zeroing needed); after the call it holds the stage
+ * results at the offsets given by qlin_moe_w4a16_workspace_layout.
+ * Errors as for qlin_moe_fp8. */
+int qlin_moe_w4a16(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                   const int32_t* topk_ids, const float* topk_w, const uint8_t* codes13,
+                   const qlin_bf16* steps13, const uint8_t* codes2, const qlin_bf16* steps2,
+                   qlin_bf16* y, void* ws, size_t ws_bytes, qlin_stream_t stream);
+
+/* Workspace bytes of qlin_moe_w4a16 (0 for a non-positive size). */
+size_t qlin_moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int topk);
+
+/* Byte offsets of its stage results (R = T*topk, row r = t*topk + j):
+ *   [0] act [R][I] bf16     [1] d [R][H] f32
+ * Returns QLIN_OK, or QLIN_ERR_ARG for a NULL out. */
+int qlin_moe_w4a16_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                                    size_t offsets[2]);
+
 #ifdef __cplusplus
 }
 #endif

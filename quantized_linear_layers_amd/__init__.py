@@ -57,6 +57,10 @@ _SIGS = {
     "qlin_moe_workspace_layout": (_INT, [_I64, _I64, _I64, _I64, _INT, C.POINTER(_SZ)]),
     "qlin_moe_fp8": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
+    "qlin_moe_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
+    "qlin_moe_w4a16_workspace_layout": (_INT, [_I64, _I64, _I64, _I64, _INT, C.POINTER(_SZ)]),
+    "qlin_moe_w4a16": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -352,3 +356,37 @@ def moe_fp8(x, topk_ids, topk_w, w13, s13, w2, s2, return_stages=False):
                   aq=view(o[3], R * I, torch.uint8).view(R, I), sa=view(o[4], R, torch.float32),
                   d=view(o[5], R * H, torch.float32).view(R, H))
     return y, stages
+
+
+def moe_w4a16(x, topk_ids, topk_w, codes13, steps13, codes2, steps2, return_stages=False):
+    """W4A16 MoE block. x [T,H] bf16; topk_ids int32 [T,k]; topk_w f32 [T,k];
+    codes13 u8 [E,2I,H/2], steps13 bf16 [E,2I,H/32]; codes2 u8 [E,H,I/2],
+    steps2 bf16 [E,H,I/32]."""
+    _check(x, "x", torch.bfloat16, 2)
+    _check(topk_ids, "topk_ids", torch.int32, 2)
+    _check(topk_w, "topk_w", torch.float32, 2)
+    _check(codes13, "codes13", torch.uint8, 3)
+    _check(steps13, "steps13", torch.bfloat16, 3)
+    _check(codes2, "codes2", torch.uint8, 3)
+    _check(steps2, "steps2", torch.bfloat16, 3)
+    T, H = x.shape
+    E, I2, H2 = codes13.shape
+    I = I2 // 2
+    topk = topk_ids.shape[1]
+    if H2 * 2 != H or codes2.shape != (E, H, I // 2) or steps13.shape != (E, I2, H // 32) or \
+            steps2.shape != (E, H, I // 32) or topk_w.shape != topk_ids.shape or topk_ids.shape[0] != T:
+        raise ValueError("shape mismatch")
+    nb = int(_lib.qlin_moe_w4a16_workspace_bytes(T, H, I, E, topk))
+    ws = workspace(nb, x.device) if not return_stages else \
+        torch.empty(max(nb, 256), dtype=torch.uint8, device=x.device)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    _call("qlin_moe_w4a16", _ptr(x), T, H, I, E, topk, _ptr(topk_ids), _ptr(topk_w), _ptr(codes13),
+          _ptr(steps13), _ptr(codes2), _ptr(steps2), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device))
+    if not return_stages:
+        return y
+    offs = (_SZ * 2)()
+    _call("qlin_moe_w4a16_workspace_layout", T, H, I, E, topk, offs)
+    R = T * topk
+    act = ws[offs[0]: offs[0] + R * I * 2].view(torch.bfloat16).view(R, I)
+    d = ws[offs[1]: offs[1] + R * H * 4].view(torch.float32).view(R, H)
+    return y, dict(act=act, d=d)

@@ -304,4 +304,39 @@ int qlin_moe_fp8(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E,
                         as_stream(stream));
 }
 
+size_t qlin_moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int topk) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return 0;
+  return moe_w4_layout(T, H, I, E, topk).total;
+}
+
+int qlin_moe_w4a16_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                                    size_t offsets[2]) {
+  QLIN_CHECK(offsets, QLIN_ERR_ARG);
+  const MoeW4Layout L = moe_w4_layout(T, H, I, E, topk);
+  offsets[0] = L.act;
+  offsets[1] = L.d;
+  return QLIN_OK;
+}
+
+int qlin_moe_w4a16(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                   const int32_t* topk_ids, const float* topk_w, const uint8_t* codes13,
+                   const qlin_bf16* steps13, const uint8_t* codes2, const qlin_bf16* steps2,
+                   qlin_bf16* y, void* ws, size_t ws_bytes, qlin_stream_t stream) {
+  QLIN_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0 && H % 32 == 0 && I % 32 == 0 &&
+                 E <= 4096 && T * topk <= 0x7FFFFFFF && topk <= E,
+             QLIN_ERR_SHAPE);
+  if (T == 0) return QLIN_OK;
+  QLIN_CHECK(x && topk_ids && topk_w && codes13 && steps13 && codes2 && steps2 && y, QLIN_ERR_ARG);
+  QLIN_CHECK(a16(x) && a16(codes13) && a16(codes2) && a16(y) && ((uintptr_t)topk_ids & 3) == 0 &&
+                 ((uintptr_t)topk_w & 3) == 0 && ((uintptr_t)steps13 & 1) == 0 &&
+                 ((uintptr_t)steps2 & 1) == 0,
+             QLIN_ERR_ALIGN);
+  QLIN_CHECK(ws && ws_bytes >= qlin_moe_w4a16_workspace_bytes(T, H, I, E, topk), QLIN_ERR_WORKSPACE);
+  QLIN_CHECK(((uintptr_t)ws & 255) == 0, QLIN_ERR_ALIGN);
+  int rc = device_ok();
+  if (rc) return rc;
+  return launch_moe_w4a16(x, T, H, I, E, topk, topk_ids, topk_w, codes13, steps13, codes2, steps2, y,
+                          ws, as_stream(stream));
+}
+
 }  // extern "C"

@@ -61,5 +61,12 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk);
 int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
                    const int32_t* ids, const float* wts, const uint8_t* w13, const float* s13,
                    const uint8_t* w2, const float* s2, uint16_t* y, void* ws, hipStream_t st);
+struct MoeW4Layout {
+  size_t act, d, off, rows, total;
+};
+MoeW4Layout moe_w4_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk);
+int launch_moe_w4a16(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                     const int32_t* ids, const float* wts, const uint8_t* p13, const uint16_t* st13,
+                     const uint8_t* p2, const uint16_t* st2, uint16_t* y, void* ws, hipStream_t st);
 
 }  // namespace qlin

@@ -14,6 +14,10 @@
 //   5. grouped down: d = (aq.w2^T)*sa*s2           -> d [R][H] fp32
 //   6. combine: y[t] = bf16(sum_j p[t,j] * d[t*topk+j]) in slot order.
 // Experts that no token routes to are never read.
+// The W4A16 block (the 4-bit builds' WNA16 expert path, "The 4-Bit Builds
+// Stay Slow") runs the same grouped GEMMs on bf16 activations and int4
+// expert banks unpacked in the kernel: no quantisation stages, and
+// act = bf16(SiLU(g) * u) is written by the gate_up epilogue.
 #include "qlin_device.h"
 #include "qlin_internal.h"
 #include "qlin_skinny.h"
@@ -36,6 +40,23 @@ MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk) {
   L.sa = take((size_t)R * 4);
   L.d = take((size_t)R * H * 4);
   L.cnt = take((size_t)E * 4);
+  L.off = take((size_t)(E + 1) * 4);
+  L.rows = take((size_t)R * 4);
+  L.total = o;
+  return L;
+}
+
+MoeW4Layout moe_w4_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk) {
+  const int64_t R = T * topk;
+  MoeW4Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes, 256);
+    return at;
+  };
+  L.act = take((size_t)R * I * 2);
+  L.d = take((size_t)R * H * 4);
   L.off = take((size_t)(E + 1) * 4);
   L.rows = take((size_t)R * 4);
   L.total = o;
@@ -89,16 +110,17 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
 
 // ---------------------------------------------------------------- grouped GEMM
 struct MoeGemmArgs {
-  const uint8_t* A;    // gate_up: xq [T][H]; down: aq [R][I]
-  const float* sa;     // gate_up: sx [T]; down: sa [R]
-  const uint8_t* W;    // gate_up: w13 [E][2I][H]; down: w2 [E][H][I]
-  const float* sw;     // s13 [E][2I] / s2 [E][H]
-  const int* off;      // [E+1]
-  const int* rows;     // [R]
+  const uint8_t* A;       // gate_up: xq [T][H] (W4A16: x bf16); down: aq [R][I] (W4A16: act bf16)
+  const float* sa;        // gate_up: sx [T]; down: sa [R] (FP8 only)
+  const uint8_t* W;       // gate_up: w13 [E][2I][H]; down: w2 [E][H][I] (W4A16: packed codes, K/2 per row)
+  const float* sw;        // s13 [E][2I] / s2 [E][H] (FP8 only)
+  const uint16_t* steps;  // W4A16 group steps [E][rows][K/32]
+  const int* off;         // [E+1]
+  const int* rows;        // [R]
   int topk;
-  int K;               // H (gate_up) or I (down)
-  int nout;            // I (gate_up: pairs) or H (down)
-  float* out;          // act [R][I] or d [R][H]
+  int K;                  // H (gate_up) or I (down)
+  int nout;               // I (gate_up: pairs) or H (down)
+  void* out;              // act [R][I] (fp32; W4A16: bf16) or d [R][H] fp32
 };
 
 // One workgroup: 64 output columns of one expert (gate_up: 64 gate
@@ -113,18 +135,22 @@ struct MoeGemmArgs {
 template <bool GATEUP>
 constexpr int moe_cols_per_wg() { return GATEUP ? 64 : 128; }
 
-template <bool GATEUP, int MB>
+template <int KIND, bool GATEUP, int MB, bool SB>
 __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int e, int rbeg, int nrows) {
+  constexpr bool W4 = KIND == kGemmW4;
+  constexpr int ESZ = W4 ? 2 : 1;
   constexpr int NB = 2;
-  constexpr int DEPTH = 4;
+  constexpr int DEPTH = W4 ? 2 : 4;
   constexpr int CW = GATEUP ? 16 : 32;  // distinct output columns per wave
+  constexpr int kPer = skinny_pieces<KIND, MB, 4>();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K;
   const int c0 = blockIdx.x * moe_cols_per_wg<GATEUP>() + wave * CW;  // this wave's first output column
   const size_t wrows = GATEUP ? 2 * (size_t)p.nout : (size_t)p.nout;
-  const uint8_t* wbase = p.W + (size_t)e * wrows * K;
+  const size_t wrow_bytes = W4 ? (size_t)K / 2 : (size_t)K;
+  const uint8_t* wbase = p.W + (size_t)e * wrows * wrow_bytes;
 
   const uint8_t* wp[NB][2];
   const uint16_t* sp[NB];
@@ -134,17 +160,22 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
     for (int h = 0; h < 2; ++h) {
       // gate_up block j: bank rows j*I + column; down block j: column 16j + ..
       const int col = min(c0 + (GATEUP ? 0 : 16 * j) + 8 * h + (lane >> 3), p.nout - 1);
-      wp[j][h] = wbase + (size_t)((GATEUP ? j * p.nout : 0) + col) * K + 16 * (lane & 7);
+      wp[j][h] = wbase + (size_t)((GATEUP ? j * p.nout : 0) + col) * wrow_bytes + 16 * (lane & 7);
     }
-    sp[j] = nullptr;
+    if constexpr (W4) {
+      const int col = min(c0 + (GATEUP ? 0 : 16 * j) + r, p.nout - 1);
+      sp[j] = p.steps + ((size_t)e * wrows + (GATEUP ? j * p.nout : 0) + col) * (K / 32);
+    } else {
+      sp[j] = nullptr;
+    }
   }
-  const uint8_t* ap[MB];
-  uint32_t am[MB];
+  const uint8_t* ap[kPer];
+  uint32_t am[kPer];
 #pragma unroll
-  for (int q = 0; q < MB; ++q) {
-    const int i = (tid + 256 * q) / 16;  // tile row of this thread's chunk piece
+  for (int q = 0; q < kPer; ++q) {
+    const int i = (tid + 256 * q) / (16 * ESZ);  // tile row of this thread's chunk piece
     const int rr = p.rows[rbeg + min(i, nrows - 1)];
-    ap[q] = p.A + (size_t)(GATEUP ? rr / p.topk : rr) * K;
+    ap[q] = p.A + (size_t)(GATEUP ? rr / p.topk : rr) * K * ESZ;
     am[q] = i < nrows ? 0xFFFFFFFFu : 0u;
   }
   v4f acc[MB][NB];
@@ -152,7 +183,7 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
-  skinny_mma<kGemmFP8, MB, NB, DEPTH>(lds, wp, sp, ap, am, K, 0, K, acc);
+  skinny_mma<KIND, MB, NB, DEPTH, SB>(lds, wp, sp, ap, am, K, 0, K, acc);
 
   // epilogue operands (output rows 4g+q of each block, this lane's column),
   // fetched after the main loop so that they hold no registers during it
@@ -164,22 +195,30 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
     for (int q = 0; q < 4; ++q) {
       const int rr = p.rows[rbeg + min(i * 16 + 4 * g + q, nrows - 1)];
       rid[i][q] = rr;
-      sav[i][q] = p.sa[GATEUP ? rr / p.topk : rr];
+      sav[i][q] = W4 ? 1.0f : p.sa[GATEUP ? rr / p.topk : rr];
     }
   if constexpr (GATEUP) {
     const int col = c0 + r, colc = min(col, p.nout - 1);
-    const float swg = p.sw[(size_t)e * wrows + colc];
-    const float swu = p.sw[(size_t)e * wrows + p.nout + colc];
+    const float swg = W4 ? 1.0f : p.sw[(size_t)e * wrows + colc];
+    const float swu = W4 ? 1.0f : p.sw[(size_t)e * wrows + p.nout + colc];
     if (col < p.nout) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (i * 16 + 4 * g + q < nrows) {
-            const float gv = (acc[i][0][q] * sav[i][q]) * swg;
-            const float uv = (acc[i][1][q] * sav[i][q]) * swu;
+            float gv, uv;
+            if constexpr (W4) {
+              gv = acc[i][0][q];
+              uv = acc[i][1][q];
+            } else {
+              gv = (acc[i][0][q] * sav[i][q]) * swg;
+              uv = (acc[i][1][q] * sav[i][q]) * swu;
+            }
             const float silu = gv / (1.0f + expf(-gv));
-            p.out[(size_t)rid[i][q] * p.nout + col] = silu * uv;
+            const size_t o = (size_t)rid[i][q] * p.nout + col;
+            if constexpr (W4) reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_bf16_rne(silu * uv);
+            else reinterpret_cast<float*>(p.out)[o] = silu * uv;
           }
         }
     }
@@ -187,13 +226,16 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       const int col = c0 + 16 * j + r;
-      const float sw = p.sw[(size_t)e * wrows + min(col, p.nout - 1)];
+      const float sw = W4 ? 1.0f : p.sw[(size_t)e * wrows + min(col, p.nout - 1)];
       if (col < p.nout) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (i * 16 + 4 * g + q < nrows) p.out[(size_t)rid[i][q] * p.nout + col] = (acc[i][j][q] * sav[i][q]) * sw;
+            if (i * 16 + 4 * g + q < nrows) {
+              const float v = W4 ? acc[i][j][q] : (acc[i][j][q] * sav[i][q]) * sw;
+              reinterpret_cast<float*>(p.out)[(size_t)rid[i][q] * p.nout + col] = v;
+            }
       }
     }
   }
@@ -205,17 +247,17 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
 // average number of rows per expert: 2 (32-row blocks) for light loads, 3
 // (48-row blocks) otherwise, so that nearly every expert is served by one
 // pass while the registers still allow two workgroups per CU.
-template <bool GATEUP, int MBMAX>
+template <int KIND, bool GATEUP, int MBMAX, bool SB>
 __global__ __launch_bounds__(256) void moe_gemm_kernel(const MoeGemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<kGemmFP8, MBMAX, 2, 1>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<KIND, MBMAX, 2, KIND == kGemmW4 ? 2 : 1>()];
   const int e = blockIdx.y;
   const int beg = p.off[e], n = p.off[e + 1] - beg;
   for (int rb = 0; rb < n; rb += 16 * MBMAX) {
     const int nr = min(16 * MBMAX, n - rb);
     const int mb = (nr + 15) / 16;
-    if (mb == 1) moe_tile<GATEUP, 1>(p, lds, e, beg + rb, nr);
-    else if (mb == 2 || MBMAX == 2) moe_tile<GATEUP, 2>(p, lds, e, beg + rb, nr);
-    else moe_tile<GATEUP, (MBMAX > 2 ? 3 : 2)>(p, lds, e, beg + rb, nr);
+    if (mb == 1) moe_tile<KIND, GATEUP, 1, SB>(p, lds, e, beg + rb, nr);
+    else if (mb == 2 || MBMAX == 2) moe_tile<KIND, GATEUP, 2, SB>(p, lds, e, beg + rb, nr);
+    else moe_tile<KIND, GATEUP, (MBMAX > 2 ? 3 : 2), SB>(p, lds, e, beg + rb, nr);
   }
 }
 
@@ -270,18 +312,69 @@ int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E
   // row blocks of 32 rows when an expert averages at most 8 routed rows,
   // else 48
   const bool light = R <= 8 * E;
-  MoeGemmArgs gu{xq, sx, w13, s13, off, rows, topk, (int)H, (int)I, act};
+  MoeGemmArgs gu{xq, sx, w13, s13, nullptr, off, rows, topk, (int)H, (int)I, act};
   const dim3 ggrid((unsigned)((I + moe_cols_per_wg<true>() - 1) / moe_cols_per_wg<true>()), (unsigned)E);
-  if (light) moe_gemm_kernel<true, 2><<<ggrid, 256, 0, st>>>(gu);
-  else moe_gemm_kernel<true, 3><<<ggrid, 256, 0, st>>>(gu);
+  if (light) moe_gemm_kernel<kGemmFP8, true, 2, false><<<ggrid, 256, 0, st>>>(gu);
+  else moe_gemm_kernel<kGemmFP8, true, 3, false><<<ggrid, 256, 0, st>>>(gu);
   if ((rc = launch_status())) return rc;
 
   if ((rc = launch_quant_rows_f32(act, R, I, aq, sa, st))) return rc;
 
-  MoeGemmArgs dn{aq, sa, w2, s2, off, rows, topk, (int)I, (int)H, dd};
+  MoeGemmArgs dn{aq, sa, w2, s2, nullptr, off, rows, topk, (int)I, (int)H, dd};
   const dim3 dgrid((unsigned)((H + moe_cols_per_wg<false>() - 1) / moe_cols_per_wg<false>()), (unsigned)E);
-  if (light) moe_gemm_kernel<false, 2><<<dgrid, 256, 0, st>>>(dn);
-  else moe_gemm_kernel<false, 3><<<dgrid, 256, 0, st>>>(dn);
+  if (light) moe_gemm_kernel<kGemmFP8, false, 2, false><<<dgrid, 256, 0, st>>>(dn);
+  else moe_gemm_kernel<kGemmFP8, false, 3, false><<<dgrid, 256, 0, st>>>(dn);
+  if ((rc = launch_status())) return rc;
+
+  const long long threads = T * (H / 4);
+  moe_combine_kernel<<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(dd, ids, wts, (int)T, topk,
+                                                                             (int)H, (int)E, y);
+  return launch_status();
+}
+
+// W4A16 block (the 4-bit MoE's WNA16 expert path: bf16 activations, group-32
+// int4 expert banks): routing bookkeeping, grouped gate_up on x itself with
+// act = bf16(SiLU(g) * u) in its epilogue, grouped down on act, combine.
+int launch_moe_w4a16(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                     const int32_t* ids, const float* wts, const uint8_t* p13, const uint16_t* st13,
+                     const uint8_t* p2, const uint16_t* st2, uint16_t* y, void* ws, hipStream_t st) {
+  const MoeW4Layout L = moe_w4_layout(T, H, I, E, topk);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  uint16_t* act = reinterpret_cast<uint16_t*>(base + L.act);
+  float* dd = reinterpret_cast<float*>(base + L.d);
+  int* off = reinterpret_cast<int*>(base + L.off);
+  int* rows = reinterpret_cast<int*>(base + L.rows);
+  const int R = (int)(T * topk);
+
+  moe_route_kernel<<<1, 1024, 2 * E * sizeof(int), st>>>(ids, R, (int)E, off, rows);
+  int rc = launch_status();
+  if (rc) return rc;
+
+  const bool light = R <= 8 * E;
+  // bulk int4 step loads need 256-element K chunks and 16-byte aligned step rows
+  auto bulk = [](const uint16_t* s, int64_t K) { return K % 256 == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0; };
+  MoeGemmArgs gu{reinterpret_cast<const uint8_t*>(x), nullptr, p13, nullptr, st13, off, rows, topk, (int)H, (int)I, act};
+  const dim3 ggrid((unsigned)((I + moe_cols_per_wg<true>() - 1) / moe_cols_per_wg<true>()), (unsigned)E);
+  const bool sg = bulk(st13, H);
+  if (light) {
+    if (sg) moe_gemm_kernel<kGemmW4, true, 2, true><<<ggrid, 256, 0, st>>>(gu);
+    else moe_gemm_kernel<kGemmW4, true, 2, false><<<ggrid, 256, 0, st>>>(gu);
+  } else {
+    if (sg) moe_gemm_kernel<kGemmW4, true, 3, true><<<ggrid, 256, 0, st>>>(gu);
+    else moe_gemm_kernel<kGemmW4, true, 3, false><<<ggrid, 256, 0, st>>>(gu);
+  }
+  if ((rc = launch_status())) return rc;
+
+  MoeGemmArgs dn{reinterpret_cast<const uint8_t*>(act), nullptr, p2, nullptr, st2, off, rows, topk, (int)I, (int)H, dd};
+  const dim3 dgrid((unsigned)((H + moe_cols_per_wg<false>() - 1) / moe_cols_per_wg<false>()), (unsigned)E);
+  const bool sd = bulk(st2, I);
+  if (light) {
+    if (sd) moe_gemm_kernel<kGemmW4, false, 2, true><<<dgrid, 256, 0, st>>>(dn);
+    else moe_gemm_kernel<kGemmW4, false, 2, false><<<dgrid, 256, 0, st>>>(dn);
+  } else {
+    if (sd) moe_gemm_kernel<kGemmW4, false, 3, true><<<dgrid, 256, 0, st>>>(dn);
+    else moe_gemm_kernel<kGemmW4, false, 3, false><<<dgrid, 256, 0, st>>>(dn);
+  }
   if ((rc = launch_status())) return rc;
 
   const long long threads = T * (H / 4);

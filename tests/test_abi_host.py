@@ -118,6 +118,26 @@ def test_moe_validation(q):
     assert list(offs) == sorted(offs) and all(o % 256 == 0 for o in offs)
 
 
+def test_moe_w4a16_validation(q):
+    lib = q.lib()
+    args = [A16] * 6  # ids, weights, codes13, steps13, codes2, steps2
+    ws = C.c_void_p(0x100000)
+    need = lib.qlin_moe_w4a16_workspace_bytes(8, 256, 128, 8, 2)
+    assert need >= 16 * 128 * 2 + 16 * 256 * 4
+    assert lib.qlin_moe_w4a16(A16, 8, 250, 128, 8, 2, *args, A16, ws, need, None) == q.ERR_SHAPE
+    assert lib.qlin_moe_w4a16(A16, 8, 256, 100, 8, 2, *args, A16, ws, need, None) == q.ERR_SHAPE
+    assert lib.qlin_moe_w4a16(A16, 8, 256, 128, 8, 9, *args, A16, ws, need, None) == q.ERR_SHAPE
+    assert lib.qlin_moe_w4a16(A16, 8, 256, 128, 8, 2, *args, A16, ws, need - 1, None) == q.ERR_WORKSPACE
+    assert lib.qlin_moe_w4a16(A16, 8, 256, 128, 8, 2, *args, A16, C.c_void_p(0x100010), need,
+                              None) == q.ERR_ALIGN
+    assert lib.qlin_moe_w4a16(A16, 0, 256, 128, 8, 2, *args, A16, ws, 0, None) == q.OK
+    assert lib.qlin_moe_w4a16(None, 8, 256, 128, 8, 2, *args, A16, ws, need, None) == q.ERR_ARG
+    offs = (C.c_size_t * 2)()
+    assert lib.qlin_moe_w4a16_workspace_layout(8, 256, 128, 8, 2, offs) == q.OK
+    assert list(offs) == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lib.qlin_moe_w4a16_workspace_layout(8, 256, 128, 8, 2, None) == q.ERR_ARG
+
+
 def test_binding_rejects_host_tensors(q):
     import torch
 

@@ -479,3 +479,94 @@ def test_moe_c5(q, oracle, c5, T):
     dd["x"], dd["ids"], dd["probs"] = d["x"][:T], d["ids"][:T], d["probs"][:T]
     tokens = None if T == 64 else np.arange(0, T, 16)
     _moe_check(q, oracle, dd, w, tokens=tokens)
+
+
+# ------------------------------------------------------------ W4A16 MoE
+def _moe_w4_weights(oracle, d):
+    """Packed codes and bf16 steps per expert, from the q4_0 repack of the
+    generator's bf16 expert banks."""
+    E, H, I = d["E"], d["H"], d["I"]
+    p13 = np.empty((E, 2 * I, H // 2), np.uint8); st13 = np.empty((E, 2 * I, H // 32), np.uint16)
+    p2 = np.empty((E, H, I // 2), np.uint8); st2 = np.empty((E, H, I // 32), np.uint16)
+    for e in range(E):
+        p13[e], st13[e], _ = oracle.repack_q4_0(d["w13_bf16"][e])
+        p2[e], st2[e], _ = oracle.repack_q4_0(d["w2_bf16"][e])
+    return p13, st13, p2, st2
+
+
+def _moe_w4_check(q, oracle, d, w, tokens=None):
+    p13, st13, p2, st2 = w
+    y, st = q.moe_w4a16(dev(d["x"]), dev(d["ids"]), dev(d["probs"]), dev(p13), dev(st13), dev(p2),
+                        dev(st2), return_stages=True)
+    y = host(y)
+    act = host(st["act"])
+    dg = host(st["d"])
+    T, topk = d["ids"].shape
+    E = p13.shape[0]
+    tok = np.arange(T) if tokens is None else tokens
+    ids, probs = d["ids"][tok], d["probs"][tok]
+    valid = (ids >= 0) & (ids < E)
+    # an expert id outside [0, E) is the same as a slot of weight zero
+    full = oracle.moe_w4a16(d["x"][tok], np.where(valid, ids, 0), np.where(valid, probs, 0.0),
+                            p13, st13, p2, st2)
+    rows = (tok[:, None] * topk + np.arange(topk)[None, :])[valid]
+    # stage 1: gate_up + SiLU(g)*u, rounded once to bf16; the two fp32 sums
+    # differ in order only, so a rounding decision may land one bf16 ulp away
+    tol_check(bf16_to_f32(act[rows]), bf16_to_f32(full["act16"][valid.ravel()]), "moe w4 act")
+    # stage 2: down projection of the GPU's own bf16 intermediate, per expert
+    # through the W4A16 GEMM oracle
+    ref_d = np.empty((len(rows), d["H"]), np.float32)
+    e_of = ids[valid]
+    for e in np.unique(e_of):
+        sel = np.flatnonzero(e_of == e)
+        ref_d[sel], _ = oracle.gemm_w4a16(act[rows[sel]], p2[e], st2[e])
+    tol_check(dg[rows], ref_d, "moe w4 down")
+    # stage 3: probability-weighted sum of the GPU's down rows in slot order
+    y32 = np.zeros((len(tok), d["H"]), np.float32)
+    for j in range(topk):
+        m = valid[:, j]
+        y32[m] += probs[m, j][:, None] * dg[tok[m] * topk + j]
+    tol_check(bf16_to_f32(y[tok]), y32, "moe w4 y")
+    # end to end against the full oracle, per element: no requantisation
+    # sits between the two GEMMs, so a bf16 rounding of the intermediate that
+    # lands one ulp away moves the output far less than the bound
+    ratio = tol_check(bf16_to_f32(y[tok]), full["y32"], "moe w4 end-to-end")
+    print(f"moe w4 end-to-end: worst error / bound {ratio:.3f}", flush=True)
+
+
+def test_moe_w4a16_small(q, oracle):
+    d = gen.moe_config(E=8, H=256, I=128, T=24, topk=2, seed=13)
+    _moe_w4_check(q, oracle, d, _moe_w4_weights(oracle, d))
+
+
+def test_moe_w4a16_ragged_and_invalid_ids(q, oracle):
+    """H and I that are not multiples of the kernel's K step, T not a
+    multiple of anything, and expert ids outside [0, E) in some slots."""
+    d = gen.moe_config(E=6, H=160, I=96, T=13, topk=3, seed=17)
+    d["ids"] = d["ids"].copy()
+    d["ids"][0, 1] = -1
+    d["ids"][5, 0] = 6
+    d["ids"][12, 2] = 1 << 30
+    _moe_w4_check(q, oracle, d, _moe_w4_weights(oracle, d))
+
+
+def test_moe_w4a16_skewed_routing(q, oracle):
+    """Every token on the same two experts: > 64 rows per expert."""
+    d = gen.moe_config(E=4, H=128, I=64, T=100, topk=2, seed=14)
+    d["ids"] = np.tile(np.int32([[2, 0]]), (100, 1))
+    _moe_w4_check(q, oracle, d, _moe_w4_weights(oracle, d))
+
+
+@pytest.fixture(scope="module")
+def c5w4(oracle, c5):
+    d, _ = c5
+    return _moe_w4_weights(oracle, d)
+
+
+@pytest.mark.parametrize("T", [64, 512])
+def test_moe_w4a16_c5(q, oracle, c5, c5w4, T):
+    d, _ = c5
+    dd = dict(d)
+    dd["x"], dd["ids"], dd["probs"] = d["x"][:T], d["ids"][:T], d["probs"][:T]
+    tokens = None if T == 64 else np.arange(0, T, 16)
+    _moe_w4_check(q, oracle, dd, c5w4, tokens=tokens)
