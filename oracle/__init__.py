@@ -57,8 +57,15 @@ def _load():
         "qo_gemm_w8a8_sample": (None, [P, P, P, P, I64, P, P, I64, P, P]),
         "qo_gemm_w4a16_sample": (None, [P, I64, P, P, I64, P, P, I64, P]),
         "qo_moe_gate_up": (None, [P, P, I64, I64, I64, C.c_int, P, P, P, P]),
+        "qo_moe_gate_up_act": (None, [P, P, I64, I64, I64, C.c_int, P, P, P, C.c_int, C.c_float,
+                                      C.c_float, C.c_float, P]),
+        "qo_quant_weight": (None, [P, I64, I64, C.c_int, P, P]),
+        "qo_swiglu_oai": (C.c_float, [C.c_float, C.c_float, C.c_float, C.c_float, C.c_float]),
+        "qo_swiglu_oai_array": (None, [P, P, I64, C.c_float, C.c_float, C.c_float, P]),
         "qo_moe_down": (None, [P, P, I64, I64, I64, C.c_int, P, P, P, P, P, P, P]),
         "qo_moe_fp8": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "qo_moe_fp8_act": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, C.c_int,
+                                  C.c_float, C.c_float, C.c_float, P, P, P, P, P, P]),
         "qo_moe_w4a16": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, P, P, P, P]),
         "qo_max_threads": (C.c_int, []),
     }
@@ -189,6 +196,37 @@ def quant_act(a_bf16, fmt: int = OCP):
     return q, s
 
 
+def quant_weight(w_bf16, fmt: int = OCP):
+    """Online per-channel quantisation of bf16 weights W [N,K]: one fp32
+    scale per output channel. Returns (codes [N,K], scales [N])."""
+    w = _c(w_bf16, np.uint16)
+    N, K = w.shape
+    q = np.empty((N, K), np.int8 if fmt == INT8 else np.uint8)
+    s = np.empty(N, np.float32)
+    _load().qo_quant_weight(_p(w), N, K, fmt, _p(q), _p(s))
+    return q, s
+
+
+def swiglu_oai(g, u, alpha: float, beta: float, limit: float):
+    """Elementwise SwiGLU-OAI of fp32 gate and up values (same shape)."""
+    g, u = _c(g, np.float32), _c(u, np.float32)
+    assert g.shape == u.shape
+    out = np.empty(g.shape, np.float32)
+    _load().qo_swiglu_oai_array(_p(g), _p(u), g.size, alpha, beta, limit, _p(out))
+    return out
+
+
+ACT_SILU, ACT_SWIGLU_OAI = 0, 1
+
+
+def _act_args(act):
+    """act None -> SiLU(g)*u; act (alpha, beta, limit) -> SwiGLU-OAI."""
+    if act is None:
+        return ACT_SILU, 1.0, 0.0, float("inf")
+    alpha, beta, limit = act
+    return ACT_SWIGLU_OAI, float(alpha), float(beta), float(limit)
+
+
 def quant_rows_f32(x, fmt: int = OCP):
     a = _c(x, np.float32)
     M, K = a.shape
@@ -269,8 +307,9 @@ def gemm_w4a16_sample(a_bf16, packed, steps, mi, ni):
 
 
 # ---------------------------------------------------------------- MoE
-def moe_fp8(x_bf16, ids, probs, w13, s13, w2, s2):
+def moe_fp8(x_bf16, ids, probs, w13, s13, w2, s2, act=None):
     """Full fp8 MoE block. w13 [E,2I,H] u8, s13 [E,2I], w2 [E,H,I] u8, s2 [E,H].
+    act: None for SiLU(g)*u, or (alpha, beta, limit) for SwiGLU-OAI.
 
     Returns dict with act32 [T*topk,I], aq, sa, d32 [T*topk,H], y32 [T,H], y16.
     """
@@ -285,21 +324,22 @@ def moe_fp8(x_bf16, ids, probs, w13, s13, w2, s2):
     out = dict(act32=np.empty((R, I), np.float32), aq=np.empty((R, I), np.uint8),
                sa=np.empty(R, np.float32), d32=np.empty((R, H), np.float32),
                y32=np.empty((T, H), np.float32), y16=np.empty((T, H), np.uint16))
-    _load().qo_moe_fp8(_p(x), T, H, I, E, topk, _p(ids), _p(probs), _p(w13), _p(s13), _p(w2),
-                       _p(s2), _p(out["act32"]), _p(out["aq"]), _p(out["sa"]), _p(out["d32"]),
+    _load().qo_moe_fp8_act(_p(x), T, H, I, E, topk, _p(ids), _p(probs), _p(w13), _p(s13), _p(w2),
+                           _p(s2), *_act_args(act), _p(out["act32"]), _p(out["aq"]), _p(out["sa"]), _p(out["d32"]),
                        _p(out["y32"]), _p(out["y16"]))
     return out
 
 
-def moe_gate_up(xq, sx, ids, w13, s13):
+def moe_gate_up(xq, sx, ids, w13, s13, act=None):
     xq, sx, ids = _c(xq, np.uint8), _c(sx, np.float32), _c(ids, np.int32)
     w13, s13 = _c(w13, np.uint8), _c(s13, np.float32)
     T, H = xq.shape
     I = w13.shape[1] // 2
     topk = ids.shape[1]
-    act = np.empty((T * topk, I), np.float32)
-    _load().qo_moe_gate_up(_p(xq), _p(sx), T, H, I, topk, _p(ids), _p(w13), _p(s13), _p(act))
-    return act
+    out = np.empty((T * topk, I), np.float32)
+    _load().qo_moe_gate_up_act(_p(xq), _p(sx), T, H, I, topk, _p(ids), _p(w13), _p(s13),
+                               *_act_args(act), _p(out))
+    return out
 
 
 def moe_down(aq, sa, ids, probs, w2, s2):

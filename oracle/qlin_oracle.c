@@ -42,6 +42,12 @@
  *   - MoE: gate rows then up rows in the fused gate_up bank; SiLU(g)*u in
  *     fp32, requantised per (token, expert) from fp32; down; combine in
  *     slot order with the router probabilities, not renormalised.
+ *   - online per-channel quantisation of bf16 weights is the per-token
+ *     activation quantiser applied to each output channel (row of W).
+ *   - SwiGLU-OAI (alpha, beta, clamp limit named by [PR], formula not on the
+ *     page) is the published form: gate clamped from above at the limit, up
+ *     clamped to [-limit, limit], act = gate * sigmoid(alpha * gate) *
+ *     (up + beta).
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,6 +60,9 @@
 #define QO_OCP 0
 #define QO_FNUZ 1
 #define QO_INT8 2
+
+#define QO_ACT_SILU 0
+#define QO_ACT_SWIGLU_OAI 1
 
 /* ------------------------------------------------------------------------ */
 /* bf16                                                                     */
@@ -431,6 +440,14 @@ void qo_quant_act(const uint16_t* a, int64_t M, int64_t K, int64_t lda, int fmt,
   }
 }
 
+/* Online per-channel weight quantisation of bf16 (non-QAT) weights ([PR]:
+ * fp8_per_channel enabled for bf16 weights, per_out_ch_quant): one scale per
+ * output channel, absmax / FMAX of that row of W [N,K], each weight encoded
+ * as w / s. The same quantiser as the per-token activations, on W's rows. */
+void qo_quant_weight(const uint16_t* w, int64_t N, int64_t K, int fmt, void* q, float* s) {
+  qo_quant_act(w, N, K, K, fmt, q, s);
+}
+
 /* Same quantiser on fp32 rows (the MoE intermediate). */
 void qo_quant_rows_f32(const float* a, int64_t M, int64_t K, int fmt, void* q, float* s) {
 #pragma omp parallel for schedule(static)
@@ -573,12 +590,37 @@ void qo_gemm_w4a16_sample(const uint16_t* a, int64_t lda, const uint8_t* packed,
 /* For token t and slot j with expert e = ids[t,j], probability p = probs:   */
 /*   h = (x_q . W13_e^T) * s_x[t] * s13[e,:]   (fp32, [2I]: gate then up)     */
 /*   act = SiLU(h[:I]) * h[I:]                 (fp32)                         */
+/*     or SwiGLU-OAI(h[:I], h[I:]) (the [PR]'s alpha/beta/limit variant)      */
 /*   (a_q, s_a) = fp8 per-row quant of act    (from fp32)                    */
 /*   d = (a_q . W2_e^T) * s_a * s2[e,:]        (fp32, [H])                    */
 /*   y[t] = bf16(sum_j p_j * d_j), slot order j = 0..topk-1.                  */
 /* Optional stage outputs (may be NULL): act32 [T*topk, I], aq [T*topk, I],  */
 /* sa [T*topk], d32 [T*topk, H], y32 [T, H]; row index t*topk + j.           */
 /* ------------------------------------------------------------------------ */
+/* SwiGLU-OAI MoE activation ([PR]: gemm1_alpha / gemm1_beta / clamp limit
+ * carried into the fused MoE; 1.702 / 1.0 for MiniMax-M3). The gate is
+ * clamped from above only, the up value to [-limit, limit]; then
+ * gate * sigmoid(alpha * gate), written g / (1 + exp(-alpha g)), times
+ * (up + beta). At alpha = 1, beta = 0 and an infinite limit this is the
+ * SiLU(g) * u expression below, operation for operation. */
+float qo_swiglu_oai(float g, float u, float alpha, float beta, float limit) {
+  if (g > limit) g = limit;
+  if (u > limit) u = limit;
+  if (u < -limit) u = -limit;
+  return (g / (1.0f + expf(-(alpha * g)))) * (u + beta);
+}
+
+void qo_swiglu_oai_array(const float* g, const float* u, int64_t n, float alpha, float beta,
+                         float limit, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = qo_swiglu_oai(g[i], u[i], alpha, beta, limit);
+}
+
+static float moe_act(int kind, float g, float u, float alpha, float beta, float limit) {
+  if (kind == QO_ACT_SWIGLU_OAI) return qo_swiglu_oai(g, u, alpha, beta, limit);
+  const float silu = g / (1.0f + expf(-g));
+  return silu * u;
+}
+
 static void moe_down_combine(const uint8_t* aq, const float* sa, int64_t T, int64_t H, int64_t I,
                              int topk, const int32_t* ids, const float* probs, const uint8_t* w2,
                              const float* s2, float* d32, float* y32, uint16_t* y16) {
@@ -604,9 +646,12 @@ static void moe_down_combine(const uint8_t* aq, const float* sa, int64_t T, int6
   }
 }
 
-void qo_moe_gate_up(const uint8_t* xq, const float* sx, int64_t T, int64_t H, int64_t I,
-                    int topk, const int32_t* ids, const uint8_t* w13, const float* s13,
-                    float* act32) {
+/* act = SiLU(g) * u (kind QO_ACT_SILU) or SwiGLU-OAI(g, u) with the given
+ * alpha, beta, limit (kind QO_ACT_SWIGLU_OAI), from the dequantised fp32
+ * gate and up values. */
+void qo_moe_gate_up_act(const uint8_t* xq, const float* sx, int64_t T, int64_t H, int64_t I,
+                        int topk, const int32_t* ids, const uint8_t* w13, const float* s13,
+                        int kind, float alpha, float beta, float limit, float* act32) {
   tables();
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < T * topk; ++r) {
@@ -616,10 +661,15 @@ void qo_moe_gate_up(const uint8_t* xq, const float* sx, int64_t T, int64_t H, in
       float u = dot_fp8(xq + t * H, w13 + (e * 2 * I + I + i) * H, H);
       g = (g * sx[t]) * s13[e * 2 * I + i];
       u = (u * sx[t]) * s13[e * 2 * I + I + i];
-      float silu = g / (1.0f + expf(-g));
-      act32[r * I + i] = silu * u;
+      act32[r * I + i] = moe_act(kind, g, u, alpha, beta, limit);
     }
   }
+}
+
+void qo_moe_gate_up(const uint8_t* xq, const float* sx, int64_t T, int64_t H, int64_t I,
+                    int topk, const int32_t* ids, const uint8_t* w13, const float* s13,
+                    float* act32) {
+  qo_moe_gate_up_act(xq, sx, T, H, I, topk, ids, w13, s13, QO_ACT_SILU, 1.0f, 0.0f, INFINITY, act32);
 }
 
 void qo_moe_down(const uint8_t* aq, const float* sa, int64_t T, int64_t H, int64_t I, int topk,
@@ -628,10 +678,11 @@ void qo_moe_down(const uint8_t* aq, const float* sa, int64_t T, int64_t H, int64
   moe_down_combine(aq, sa, T, H, I, topk, ids, probs, w2, s2, d32, y32, y16);
 }
 
-void qo_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
-                const int32_t* ids, const float* probs, const uint8_t* w13, const float* s13,
-                const uint8_t* w2, const float* s2, float* act32, uint8_t* aq, float* sa,
-                float* d32, float* y32, uint16_t* y16) {
+void qo_moe_fp8_act(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                    const int32_t* ids, const float* probs, const uint8_t* w13, const float* s13,
+                    const uint8_t* w2, const float* s2, int kind, float alpha, float beta,
+                    float limit, float* act32, uint8_t* aq, float* sa, float* d32, float* y32,
+                    uint16_t* y16) {
   (void)E;
   int64_t R = T * topk;
   uint8_t* xq = (uint8_t*)malloc((size_t)(T * H));
@@ -640,7 +691,7 @@ void qo_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, i
   uint8_t* q = aq ? aq : (uint8_t*)malloc((size_t)(R * I));
   float* s = sa ? sa : (float*)malloc((size_t)R * sizeof(float));
   qo_quant_act(x, T, H, H, QO_OCP, xq, sx);
-  qo_moe_gate_up(xq, sx, T, H, I, topk, ids, w13, s13, act);
+  qo_moe_gate_up_act(xq, sx, T, H, I, topk, ids, w13, s13, kind, alpha, beta, limit, act);
   qo_quant_rows_f32(act, R, I, QO_OCP, q, s);
   moe_down_combine(q, s, T, H, I, topk, ids, probs, w2, s2, d32, y32, y16);
   if (!act32) free(act);
@@ -648,6 +699,14 @@ void qo_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, i
   if (!sa) free(s);
   free(xq);
   free(sx);
+}
+
+void qo_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                const int32_t* ids, const float* probs, const uint8_t* w13, const float* s13,
+                const uint8_t* w2, const float* s2, float* act32, uint8_t* aq, float* sa,
+                float* d32, float* y32, uint16_t* y16) {
+  qo_moe_fp8_act(x, T, H, I, E, topk, ids, probs, w13, s13, w2, s2, QO_ACT_SILU, 1.0f, 0.0f,
+                 INFINITY, act32, aq, sa, d32, y32, y16);
 }
 
 /* ------------------------------------------------------------------------ */

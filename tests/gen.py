@@ -65,6 +65,18 @@ def qat_grid(rng: np.random.Generator, n: int, k: int):
     return codes, steps, w_bf16
 
 
+def dense_bf16(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
+    """One non-QAT bf16 weight [n,k] (bits): N(0,1) entries times a per-row
+    lognormal magnitude around 0.02, so that the output channels differ in
+    scale as trained channels do, with 0.1 % of entries scaled by 8 (heavy
+    tails set each channel's absmax)."""
+    w = rng.standard_normal(size=(n, k), dtype=np.float32)
+    w *= rng.lognormal(np.log(0.02), 0.3, size=(n, 1)).astype(np.float32)
+    mask = rng.random(size=(n, k), dtype=np.float32) < 0.001
+    w[mask] *= 8.0
+    return to_bf16_bits(w)
+
+
 def activations(rng: np.random.Generator, m: int, k: int) -> np.ndarray:
     """bf16 bits [m,k]: N(0,1) with 1 % of entries scaled by 20."""
     x = rng.standard_normal(size=(m, k), dtype=np.float32)
@@ -172,3 +184,26 @@ def moe_config(E: int | None = None, H: int | None = None, I: int | None = None,
     return dict(E=E, H=H, I=I, T=T, topk=topk, codes13=c13, steps13=s13, w13_bf16=w13,
                 codes2=c2, steps2=s2, w2_bf16=w2, x=x, logits=logits, ids=ids, probs=probs)
 
+
+def moe_bf16_config(E: int | None = None, H: int | None = None, I: int | None = None,
+                    T: int | None = None, topk: int | None = None, seed: int | None = None):
+    """A bf16 (non-QAT) MoE block of configuration 5's shape: the expert
+    banks are dense_bf16 weights, quantised per channel on line. Returns
+    w13_bf16 [E, 2I, H], w2_bf16 [E, H, I], x [T,H], ids/probs [T,topk]."""
+    c = CONFIGS[5]
+    E = c["E"] if E is None else E
+    H = c["H"] if H is None else H
+    I = c["I"] if I is None else I
+    T = max(c["T"]) if T is None else T
+    topk = c["topk"] if topk is None else topk
+    rng = np.random.default_rng((c["seed"] + 100) if seed is None else seed)
+    w13 = np.empty((E, 2 * I, H), np.uint16)
+    w2 = np.empty((E, H, I), np.uint16)
+    for e in range(E):
+        w13[e] = dense_bf16(rng, 2 * I, H)
+        w2[e] = dense_bf16(rng, H, I)
+    x = activations(rng, T, H)
+    logits = rng.standard_normal(size=(T, E), dtype=np.float32)
+    ids, probs = route_topk(logits, topk)
+    return dict(E=E, H=H, I=I, T=T, topk=topk, w13_bf16=w13, w2_bf16=w2, x=x, logits=logits,
+                ids=ids, probs=probs)
