@@ -405,6 +405,35 @@ def c5_rows(q, torch, gen, iters):
                                            frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
     del copies, c13, c2
     torch.cuda.empty_cache()
+    # bf16 (non-QAT) banks quantised per channel on line, then the FP8 block
+    # with the SwiGLU-OAI activation (alpha 1.702, beta 1.0, clamp 7.0)
+    d = gen.moe_bf16_config()
+    b13 = dev(d["w13_bf16"].reshape(E * 2 * I, H), torch)
+    b2 = dev(d["w2_bf16"].reshape(E * H, I), torch)
+    tq = T.time(lambda i: (q.quant_weight(b13), q.quant_weight(b2)), max(4, iters // 8), filler_ms=5)
+    qb = (b13.numel() + b2.numel()) * 3 + 4 * (E * 2 * I + E * H)
+    rows["C5_quant_weight_bf16_banks"] = dict(us=round(tq["mean_us"], 1), bytes=qb,
+                                              GBps=round(qb / (tq["mean_us"] * 1e3), 1))
+    w13, s13 = q.quant_weight(b13)
+    w2, s2 = q.quant_weight(b2)
+    del b13, b2
+    w13, s13, w2, s2 = w13.view(E, 2 * I, H), s13.view(E, 2 * I), w2.view(E, H, I), s2.view(E, H)
+    copies = [(w13, s13, w2, s2)] + [(w13.clone(), s13.clone(), w2.clone(), s2.clone())
+                                     for _ in range(2)]
+    for Tn in (64, 512):
+        x = dev(d["x"][:Tn], torch)
+        ids = dev(d["ids"][:Tn], torch)
+        pr = dev(d["probs"][:Tn], torch)
+        touched = len(set(d["ids"][:Tn].ravel().tolist()))
+        wb = touched * (2 * I * H + 4 * 2 * I + H * I + 4 * H)
+        t = T.time(lambda i: q.moe_fp8(x, ids, pr, *copies[i % len(copies)],
+                                       swiglu_oai=(1.702, 1.0, 7.0)), max(6, iters // 4), filler_ms=5)
+        gbs = wb / (t["mean_us"] * 1e3)
+        rows[f"C5_moe_fp8_swiglu_oai_T{Tn}"] = dict(us=round(t["mean_us"], 1), experts_touched=touched,
+                                                    weight_bytes=wb, GBps=round(gbs, 1),
+                                                    frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+    del copies, w13, w2
+    torch.cuda.empty_cache()
     return rows
 
 

@@ -155,6 +155,15 @@ int qlin_dequant_q4_bf16(const uint8_t* codes, const qlin_bf16* steps, int64_t N
 int qlin_quant_act(const qlin_bf16* a, int64_t M, int64_t K, int64_t lda, int fmt, void* a_q,
                    float* a_scale, qlin_stream_t stream);
 
+/* Online per-channel quantisation of bf16 (non-QAT) weights ([PR]:
+ * fp8_per_channel enabled for bf16 weights on the GPU, one scale per output
+ * channel): each row n of W [N][K] gets w_scale[n] = max_k |w[n,k]| / FMAX
+ * and codes enc(w / w_scale[n]), exactly qlin_quant_act on W's rows (FMAX
+ * 448 QLIN_E4M3, 240 QLIN_E4M3FNUZ, 127 QLIN_INT8). w [N][K] bf16, K % 16
+ * == 0; w_q [N][K] bytes; w_scale [N] fp32. Errors as for qlin_quant_act. */
+int qlin_quant_weight(const qlin_bf16* w, int64_t N, int64_t K, int fmt, void* w_q, float* w_scale,
+                      qlin_stream_t stream);
+
 /* Element-wise fp32 -> FP8 encoder (nearest even, saturating), the codec the
  * quantisers use. fmt: QLIN_E4M3 or QLIN_E4M3FNUZ. x, out: n elements. */
 int qlin_fp8_encode_f32(const float* x, int64_t n, int fmt, uint8_t* out, qlin_stream_t stream);
@@ -245,7 +254,20 @@ int qlin_moe_fp8(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E,
                  const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y, void* ws,
                  size_t ws_bytes, qlin_stream_t stream);
 
-/* Workspace bytes of qlin_moe_fp8. */
+/* The same block with the SwiGLU-OAI activation in place of SiLU(g) * u
+ * ([PR]: the fp8 MoE config carries gemm1_alpha / gemm1_beta, 1.702 / 1.0
+ * for MiniMax-M3, and a clamp limit):
+ *   g' = min(g, limit); u' = min(max(u, -limit), limit);
+ *   act = g' * sigmoid(alpha * g') * (u' + beta)   (fp32).
+ * alpha and beta finite, limit > 0 (+inf: no clamp), else QLIN_ERR_ARG.
+ * Arguments, workspace and stage results as for qlin_moe_fp8. */
+int qlin_moe_fp8_swiglu_oai(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                            const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                            const float* s13, const uint8_t* w2, const float* s2, float alpha,
+                            float beta, float limit, qlin_bf16* y, void* ws, size_t ws_bytes,
+                            qlin_stream_t stream);
+
+/* Workspace bytes of qlin_moe_fp8 and qlin_moe_fp8_swiglu_oai. */
 size_t qlin_moe_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int topk);
 
 /* Byte offsets of the MoE stage results inside its workspace (R = T*topk):

@@ -45,6 +45,7 @@ _SIGS = {
     "qlin_fp8_fnuz_to_ocp": (_INT, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
     "qlin_dequant_q4_bf16": (_INT, [_P, _P, _I64, _I64, _P, _P]),
     "qlin_quant_act": (_INT, [_P, _I64, _I64, _I64, _INT, _P, _P, _P]),
+    "qlin_quant_weight": (_INT, [_P, _I64, _I64, _INT, _P, _P, _P]),
     "qlin_fp8_encode_f32": (_INT, [_P, _I64, _INT, _P, _P]),
     "qlin_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     "qlin_workspace_init": (_INT, [_P, _SZ, _P]),
@@ -57,6 +58,8 @@ _SIGS = {
     "qlin_moe_workspace_layout": (_INT, [_I64, _I64, _I64, _I64, _INT, C.POINTER(_SZ)]),
     "qlin_moe_fp8": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
+    "qlin_moe_fp8_swiglu_oai": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P,
+                                       C.c_float, C.c_float, C.c_float, _P, _P, _SZ, _P]),
     "qlin_moe_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
     "qlin_moe_w4a16_workspace_layout": (_INT, [_I64, _I64, _I64, _I64, _INT, C.POINTER(_SZ)]),
     "qlin_moe_w4a16": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -320,9 +323,22 @@ def moe_workspace_layout(T, H, I, E, topk):
     return [int(o) for o in offs]
 
 
-def moe_fp8(x, topk_ids, topk_w, w13, s13, w2, s2, return_stages=False):
+def quant_weight(w: torch.Tensor, fmt="e4m3"):
+    """Online per-channel quantisation of a bf16 weight [N,K] (contiguous):
+    (codes [N,K], scale f32 [N]), one scale per output channel."""
+    _check(w, "w", torch.bfloat16, 2)
+    N, K = w.shape
+    f = _FMT[fmt]
+    q = torch.empty((N, K), dtype=torch.int8 if f == INT8 else torch.uint8, device=w.device)
+    s = torch.empty(N, dtype=torch.float32, device=w.device)
+    _call("qlin_quant_weight", _ptr(w), N, K, f, _ptr(q), _ptr(s), _stream(w.device))
+    return q, s
+
+
+def moe_fp8(x, topk_ids, topk_w, w13, s13, w2, s2, return_stages=False, swiglu_oai=None):
     """FP8 MoE block. x [T,H] bf16; topk_ids int32 [T,k]; topk_w f32 [T,k];
-    w13 u8 [E,2I,H], s13 f32 [E,2I]; w2 u8 [E,H,I], s2 f32 [E,H]."""
+    w13 u8 [E,2I,H], s13 f32 [E,2I]; w2 u8 [E,H,I], s2 f32 [E,H].
+    swiglu_oai: None for SiLU(g)*u, or (alpha, beta, limit) for SwiGLU-OAI."""
     _check(x, "x", torch.bfloat16, 2)
     _check(topk_ids, "topk_ids", torch.int32, 2)
     _check(topk_w, "topk_w", torch.float32, 2)
@@ -341,8 +357,14 @@ def moe_fp8(x, topk_ids, topk_w, w13, s13, w2, s2, return_stages=False):
     ws = workspace(nb, x.device) if not return_stages else \
         torch.empty(max(nb, 256), dtype=torch.uint8, device=x.device)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    _call("qlin_moe_fp8", _ptr(x), T, H, I, E, topk, _ptr(topk_ids), _ptr(topk_w), _ptr(w13),
-          _ptr(s13), _ptr(w2), _ptr(s2), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device))
+    if swiglu_oai is None:
+        _call("qlin_moe_fp8", _ptr(x), T, H, I, E, topk, _ptr(topk_ids), _ptr(topk_w), _ptr(w13),
+              _ptr(s13), _ptr(w2), _ptr(s2), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device))
+    else:
+        alpha, beta, limit = (float(v) for v in swiglu_oai)
+        _call("qlin_moe_fp8_swiglu_oai", _ptr(x), T, H, I, E, topk, _ptr(topk_ids), _ptr(topk_w),
+              _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), alpha, beta, limit, _ptr(y), _ptr(ws),
+              ws.numel(), _stream(x.device))
     if not return_stages:
         return y
     o = moe_workspace_layout(T, H, I, E, topk)

@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #include "qlin_internal.h"
+#include <cmath>
 
 namespace qlin {
 
@@ -140,6 +141,12 @@ int qlin_quant_act(const qlin_bf16* a, int64_t M, int64_t K, int64_t lda, int fm
   int rc = device_ok();
   if (rc) return rc;
   return launch_quant_act(a, M, K, lda, fmt, a_q, a_scale, as_stream(stream));
+}
+
+int qlin_quant_weight(const qlin_bf16* w, int64_t N, int64_t K, int fmt, void* w_q, float* w_scale,
+                      qlin_stream_t stream) {
+  // one output channel = one row of W: the per-row quantiser of the activations
+  return qlin_quant_act(w, N, K, K, fmt, w_q, w_scale, stream);
 }
 
 int qlin_fp8_encode_f32(const float* x, int64_t n, int fmt, uint8_t* out, qlin_stream_t stream) {
@@ -283,10 +290,10 @@ int qlin_moe_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t E, int to
   return QLIN_OK;
 }
 
-int qlin_moe_fp8(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
-                 const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
-                 const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y, void* ws,
-                 size_t ws_bytes, qlin_stream_t stream) {
+static int moe_fp8_call(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                        const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                        const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y,
+                        void* ws, size_t ws_bytes, qlin_stream_t stream, const MoeAct& act) {
   QLIN_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0 && H % 32 == 0 && I % 32 == 0 &&
                  E <= 4096 && T * topk <= 0x7FFFFFFF && topk <= E,
              QLIN_ERR_SHAPE);
@@ -301,7 +308,30 @@ int qlin_moe_fp8(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E,
   int rc = device_ok();
   if (rc) return rc;
   return launch_moe_fp8(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y, ws,
-                        as_stream(stream));
+                        as_stream(stream), act);
+}
+
+int qlin_moe_fp8(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                 const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                 const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y, void* ws,
+                 size_t ws_bytes, qlin_stream_t stream) {
+  return moe_fp8_call(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y, ws, ws_bytes,
+                      stream, MoeAct{});
+}
+
+int qlin_moe_fp8_swiglu_oai(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                            const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                            const float* s13, const uint8_t* w2, const float* s2, float alpha,
+                            float beta, float limit, qlin_bf16* y, void* ws, size_t ws_bytes,
+                            qlin_stream_t stream) {
+  QLIN_CHECK(std::isfinite(alpha) && std::isfinite(beta) && limit > 0.0f, QLIN_ERR_ARG);
+  MoeAct act;
+  act.kind = kMoeActSwigluOai;
+  act.alpha = alpha;
+  act.beta = beta;
+  act.limit = limit;
+  return moe_fp8_call(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y, ws, ws_bytes,
+                      stream, act);
 }
 
 size_t qlin_moe_w4a16_workspace_bytes(int64_t T, int64_t H, int64_t I, int64_t E, int topk) {

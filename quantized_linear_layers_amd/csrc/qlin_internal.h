@@ -54,13 +54,23 @@ int launch_gemm(int kind, const void* a, int64_t lda, const float* sa, const voi
                 size_t ws_bytes, hipStream_t st);
 
 // ---- MoE (qlin_moe.hip)
+// Activation of the gate_up epilogue: SiLU(g) * u, or SwiGLU-OAI (gate
+// clamped from above at limit, up to [-limit, limit], then
+// g * sigmoid(alpha g) * (u + beta)).
+constexpr int kMoeActSilu = 0;
+constexpr int kMoeActSwigluOai = 1;
+struct MoeAct {
+  int kind = kMoeActSilu;
+  float alpha = 1.0f, beta = 0.0f, limit = __builtin_inff();
+};
 struct MoeLayout {
   size_t xq, sx, act, aq, sa, d, cnt, off, rows, total;
 };
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk);
 int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
                    const int32_t* ids, const float* wts, const uint8_t* w13, const float* s13,
-                   const uint8_t* w2, const float* s2, uint16_t* y, void* ws, hipStream_t st);
+                   const uint8_t* w2, const float* s2, uint16_t* y, void* ws, hipStream_t st,
+                   const MoeAct& act = MoeAct{});
 struct MoeW4Layout {
   size_t act, d, off, rows, total;
 };

@@ -10,6 +10,8 @@
 //   3. grouped gate_up: for every touched expert, its 2I x H FP8 weights are
 //      streamed once for all of its rows; h = (xq.w13^T)*sx*s13, then
 //      act = SiLU(h[:I]) * h[I:] in fp32        -> act [R][I]   (R = T*topk)
+//      (or the SwiGLU-OAI activation with alpha, beta and a clamp limit, the
+//      variant the PR carries into the fp8 MoE config)
 //   4. per-row FP8 requant of act                 -> aq [R][I], sa [R]
 //   5. grouped down: d = (aq.w2^T)*sa*s2           -> d [R][H] fp32
 //   6. combine: y[t] = bf16(sum_j p[t,j] * d[t*topk+j]) in slot order.
@@ -121,7 +123,21 @@ struct MoeGemmArgs {
   int K;                  // H (gate_up) or I (down)
   int nout;               // I (gate_up: pairs) or H (down)
   void* out;              // act [R][I] (fp32; W4A16: bf16) or d [R][H] fp32
+  MoeAct act;             // gate_up epilogue activation
 };
+
+// gate_up epilogue: SiLU(g) * u, or SwiGLU-OAI with the call's alpha, beta
+// and clamp limit (the same expression order as the SiLU form, so alpha 1,
+// beta 0 and an infinite limit give SiLU(g) * u).
+__device__ __forceinline__ float moe_activation(const MoeAct& a, float g, float u) {
+  if (a.kind == kMoeActSwigluOai) {
+    g = fminf(g, a.limit);
+    u = fminf(fmaxf(u, -a.limit), a.limit);
+    return (g / (1.0f + expf(-(a.alpha * g)))) * (u + a.beta);
+  }
+  const float silu = g / (1.0f + expf(-g));
+  return silu * u;
+}
 
 // One workgroup: 64 output columns of one expert (gate_up: 64 gate
 // columns and the matching 64 up columns of the bank), for up to MB*16 of
@@ -215,10 +231,10 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
               gv = (acc[i][0][q] * sav[i][q]) * swg;
               uv = (acc[i][1][q] * sav[i][q]) * swu;
             }
-            const float silu = gv / (1.0f + expf(-gv));
+            const float av = moe_activation(p.act, gv, uv);
             const size_t o = (size_t)rid[i][q] * p.nout + col;
-            if constexpr (W4) reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_bf16_rne(silu * uv);
-            else reinterpret_cast<float*>(p.out)[o] = silu * uv;
+            if constexpr (W4) reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_bf16_rne(av);
+            else reinterpret_cast<float*>(p.out)[o] = av;
           }
         }
     }
@@ -291,12 +307,13 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
 
 int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
                    const int32_t* ids, const float* wts, const uint8_t* w13, const float* s13,
-                   const uint8_t* w2, const float* s2, uint16_t* y, void* ws, hipStream_t st) {
+                   const uint8_t* w2, const float* s2, uint16_t* y, void* ws, hipStream_t st,
+                   const MoeAct& act) {
   const MoeLayout L = moe_layout(T, H, I, E, topk);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   uint8_t* xq = base + L.xq;
   float* sx = reinterpret_cast<float*>(base + L.sx);
-  float* act = reinterpret_cast<float*>(base + L.act);
+  float* act32 = reinterpret_cast<float*>(base + L.act);
   uint8_t* aq = base + L.aq;
   float* sa = reinterpret_cast<float*>(base + L.sa);
   float* dd = reinterpret_cast<float*>(base + L.d);
@@ -312,13 +329,13 @@ int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E
   // row blocks of 32 rows when an expert averages at most 8 routed rows,
   // else 48
   const bool light = R <= 8 * E;
-  MoeGemmArgs gu{xq, sx, w13, s13, nullptr, off, rows, topk, (int)H, (int)I, act};
+  MoeGemmArgs gu{xq, sx, w13, s13, nullptr, off, rows, topk, (int)H, (int)I, act32, act};
   const dim3 ggrid((unsigned)((I + moe_cols_per_wg<true>() - 1) / moe_cols_per_wg<true>()), (unsigned)E);
   if (light) moe_gemm_kernel<kGemmFP8, true, 2, false><<<ggrid, 256, 0, st>>>(gu);
   else moe_gemm_kernel<kGemmFP8, true, 3, false><<<ggrid, 256, 0, st>>>(gu);
   if ((rc = launch_status())) return rc;
 
-  if ((rc = launch_quant_rows_f32(act, R, I, aq, sa, st))) return rc;
+  if ((rc = launch_quant_rows_f32(act32, R, I, aq, sa, st))) return rc;
 
   MoeGemmArgs dn{aq, sa, w2, s2, nullptr, off, rows, topk, (int)I, (int)H, dd};
   const dim3 dgrid((unsigned)((H + moe_cols_per_wg<false>() - 1) / moe_cols_per_wg<false>()), (unsigned)E);

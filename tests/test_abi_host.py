@@ -102,6 +102,10 @@ def test_repack_quant_validation(q):
     assert lib.qlin_quant_act(A16, 4, 64, 64, 9, A16, A16, None) == q.ERR_ARG
     assert lib.qlin_quant_act(A16, 0, 64, 64, 0, A16, A16, None) == q.OK
     assert lib.qlin_fp8_encode_f32(A16, 16, 2, A16, None) == q.ERR_ARG
+    assert lib.qlin_quant_weight(A16, 16, 40, 0, A16, A16, None) == q.ERR_SHAPE  # K % 16
+    assert lib.qlin_quant_weight(A16, 16, 64, 9, A16, A16, None) == q.ERR_ARG
+    assert lib.qlin_quant_weight(A_ODD, 16, 64, 1, A16, A16, None) == q.ERR_ALIGN
+    assert lib.qlin_quant_weight(A16, 0, 64, 0, A16, A16, None) == q.OK
 
 
 def test_moe_validation(q):
@@ -116,6 +120,22 @@ def test_moe_validation(q):
     offs = (C.c_size_t * 6)()
     assert lib.qlin_moe_workspace_layout(8, 256, 128, 8, 2, offs) == q.OK
     assert list(offs) == sorted(offs) and all(o % 256 == 0 for o in offs)
+
+
+def test_moe_swiglu_oai_validation(q):
+    lib = q.lib()
+    args = [A16] * 6  # ids, weights, w13, s13, w2, s2
+    ws = C.c_void_p(0x100000)
+    need = lib.qlin_moe_workspace_bytes(8, 256, 128, 8, 2)
+    f = lib.qlin_moe_fp8_swiglu_oai
+    ok = (1.702, 1.0, 7.0)
+    for bad in ((float("nan"), 1.0, 7.0), (1.702, float("inf"), 7.0), (1.702, 1.0, 0.0),
+                (1.702, 1.0, -1.0), (1.702, 1.0, float("nan"))):
+        assert f(A16, 8, 256, 128, 8, 2, *args, *bad, A16, ws, need, None) == q.ERR_ARG
+    assert f(A16, 8, 250, 128, 8, 2, *args, *ok, A16, ws, need, None) == q.ERR_SHAPE
+    assert f(A16, 8, 256, 128, 8, 2, *args, *ok, A16, ws, need - 1, None) == q.ERR_WORKSPACE
+    assert f(A16, 8, 256, 128, 8, 2, *args, *ok, A16, C.c_void_p(0x100010), need, None) == q.ERR_ALIGN
+    assert f(A16, 0, 256, 128, 8, 2, *args, 1.702, 1.0, float("inf"), A16, ws, 0, None) == q.OK
 
 
 def test_moe_w4a16_validation(q):

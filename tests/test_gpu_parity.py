@@ -417,10 +417,11 @@ def _moe_weights(oracle, d):
     return w13, s13, w2, s2
 
 
-def _moe_check(q, oracle, d, w, tokens=None):
+def _moe_check(q, oracle, d, w, tokens=None, act=None):
+    """act: None (SiLU(g)*u) or (alpha, beta, limit) for SwiGLU-OAI."""
     w13, s13, w2, s2 = w
     y, st = q.moe_fp8(dev(d["x"]), dev(d["ids"]), dev(d["probs"]), dev(w13), dev(s13), dev(w2),
-                      dev(s2), return_stages=True)
+                      dev(s2), return_stages=True, swiglu_oai=act)
     y = host(y)
     st = {k: host(v) for k, v in st.items()}
     T, topk = d["ids"].shape
@@ -430,8 +431,8 @@ def _moe_check(q, oracle, d, w, tokens=None):
     xq, sx = oracle.quant_act(d["x"][tok], OCP)
     assert np.array_equal(st["xq"][tok], xq) and np.array_equal(st["sx"][tok], sx)
     # stage 1: gate_up + SiLU(g)*u on identical quantised tokens
-    act = oracle.moe_gate_up(xq, sx, d["ids"][tok], w13, s13)
-    tol_check(st["act"][rows], act, "moe act")
+    a_ref = oracle.moe_gate_up(xq, sx, d["ids"][tok], w13, s13, act=act)
+    tol_check(st["act"][rows], a_ref, "moe act")
     # stage 2: requantisation of the GPU's own fp32 intermediate, bit-exact
     aq, sa = oracle.quant_rows_f32(st["act"][rows], OCP)
     assert np.array_equal(st["aq"][rows], aq) and np.array_equal(st["sa"][rows], sa)
@@ -444,7 +445,7 @@ def _moe_check(q, oracle, d, w, tokens=None):
     # libm exp) moves a whole token row slightly, so the end-to-end check is
     # a relative RMS bound plus the share of elements inside the per-element
     # bound, both printed.
-    full = oracle.moe_fp8(d["x"][tok], d["ids"][tok], d["probs"][tok], w13, s13, w2, s2)
+    full = oracle.moe_fp8(d["x"][tok], d["ids"][tok], d["probs"][tok], w13, s13, w2, s2, act=act)
     g = bf16_to_f32(y[tok]).astype(np.float64)
     r = full["y32"].astype(np.float64)
     rms = np.sqrt(np.mean(r ** 2))
@@ -570,3 +571,72 @@ def test_moe_w4a16_c5(q, oracle, c5, c5w4, T):
     dd["x"], dd["ids"], dd["probs"] = d["x"][:T], d["ids"][:T], d["probs"][:T]
     tokens = None if T == 64 else np.arange(0, T, 16)
     _moe_w4_check(q, oracle, dd, c5w4, tokens=tokens)
+
+
+# ------------------------------------------ online per-channel FP8 + SwiGLU-OAI
+ALPHA, BETA = 1.702, 1.0
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e4m3fnuz", "int8"])
+@pytest.mark.parametrize("shape", [(300, 2048), (77, 80), (5, 16400)], ids=["k2048", "k80", "k16400"])
+def test_quant_weight_bitexact(q, oracle, fmt, shape):
+    """Per-channel quantisation of non-QAT bf16 weights, every code and scale
+    (K = 16400 takes the two-pass path for rows longer than 16384)."""
+    N, K = shape
+    w = gen.dense_bf16(np.random.default_rng(N + K), N, K)
+    f = {"e4m3": 0, "e4m3fnuz": 1, "int8": 2}[fmt]
+    qo, so = oracle.quant_weight(w, f)
+    qg, sg = q.quant_weight(dev(w), fmt)
+    qg = host(qg.view(torch.uint8) if fmt == "int8" else qg)
+    assert np.array_equal(qg, qo.view(np.uint8)) and np.array_equal(host(sg), so)
+
+
+def _online_weights(oracle, d):
+    """Per-channel FP8 of the bf16 expert banks, by the oracle."""
+    E, H, I = d["E"], d["H"], d["I"]
+    w13, s13 = oracle.quant_weight(d["w13_bf16"].reshape(E * 2 * I, H), 0)
+    w2, s2 = oracle.quant_weight(d["w2_bf16"].reshape(E * H, I), 0)
+    return w13.reshape(E, 2 * I, H), s13.reshape(E, 2 * I), w2.reshape(E, H, I), s2.reshape(E, H)
+
+
+def test_moe_swiglu_oai_small(q, oracle):
+    """Gate and up values are ~0.4 at H = 256: a limit of 0.4 clamps often."""
+    d = gen.moe_bf16_config(E=8, H=256, I=128, T=24, topk=2, seed=61)
+    _moe_check(q, oracle, d, _online_weights(oracle, d), act=(ALPHA, BETA, 0.4))
+
+
+def test_moe_swiglu_oai_unclamped_is_silu(q, oracle):
+    """alpha 1, beta 0, no clamp through the SwiGLU-OAI entry point gives the
+    SiLU block's output bit for bit."""
+    d = gen.moe_bf16_config(E=8, H=256, I=128, T=24, topk=2, seed=62)
+    w = [dev(a) for a in _online_weights(oracle, d)]
+    x, ids, pr = dev(d["x"]), dev(d["ids"]), dev(d["probs"])
+    a = host(q.moe_fp8(x, ids, pr, *w))
+    b = host(q.moe_fp8(x, ids, pr, *w, swiglu_oai=(1.0, 0.0, float("inf"))))
+    assert np.array_equal(a, b)
+
+
+@pytest.fixture(scope="module")
+def c5_online(oracle):
+    d = gen.moe_bf16_config()
+    return d, _online_weights(oracle, d)
+
+
+def test_quant_weight_c5_banks(q, c5_online):
+    """The GPU's per-channel FP8 of the full bf16 expert banks equals the
+    oracle's, every code and scale."""
+    d, (w13, s13, w2, s2) = c5_online
+    E, H, I = d["E"], d["H"], d["I"]
+    for wb, wq, ws, shape in ((d["w13_bf16"], w13, s13, (E * 2 * I, H)), (d["w2_bf16"], w2, s2, (E * H, I))):
+        qg, sg = q.quant_weight(dev(wb.reshape(shape)), "e4m3")
+        assert np.array_equal(host(qg), wq.reshape(shape)) and np.array_equal(host(sg), ws.ravel())
+        del qg, sg
+
+
+@pytest.mark.parametrize("T", [64, 512])
+def test_moe_swiglu_oai_c5(q, oracle, c5_online, T):
+    d, w = c5_online
+    dd = dict(d)
+    dd["x"], dd["ids"], dd["probs"] = d["x"][:T], d["ids"][:T], d["probs"][:T]
+    tokens = None if T == 64 else np.arange(0, T, 16)
+    _moe_check(q, oracle, dd, w, tokens=tokens, act=(ALPHA, BETA, 7.0))
