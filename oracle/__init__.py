@@ -67,6 +67,7 @@ def _load():
         "qo_moe_fp8_act": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, C.c_int,
                                   C.c_float, C.c_float, C.c_float, P, P, P, P, P, P]),
         "qo_moe_w4a16": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, P, P, P, P]),
+        "qo_embed_q4": (None, [P, I64, P, P, I64, I64, P]),
         "qo_max_threads": (C.c_int, []),
     }
     for name, (res, args) in sig.items():
@@ -374,6 +375,17 @@ def moe_w4a16(x_bf16, ids, probs, p13, st13, p2, st2):
                y32=np.empty((T, H), np.float32), y16=np.empty((T, H), np.uint16))
     _load().qo_moe_w4a16(_p(x), T, H, I, E, topk, _p(ids), _p(probs), _p(p13), _p(st13), _p(p2),
                          _p(st2), _p(out["act16"]), _p(out["d32"]), _p(out["y32"]), _p(out["y16"]))
+    return out
+
+
+def embed_q4(ids, packed, steps):
+    """Rows ids [T] of an int4 table (packed [V,D/2] u8, steps [V,D/32] bf16)
+    as bf16 bits [T,D]; ids outside [0,V) give zero rows."""
+    ids, p, s = _c(ids, np.int32), _c(packed, np.uint8), _c(steps, np.uint16)
+    V, D2 = p.shape
+    D = 2 * D2
+    out = np.empty((ids.size, D), np.uint16)
+    _load().qo_embed_q4(_p(ids), ids.size, _p(p), _p(s), V, D, _p(out))
     return out
 
 

@@ -710,6 +710,26 @@ void qo_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E, i
 }
 
 /* ------------------------------------------------------------------------ */
+/* int4 vocabulary table lookup ([E2B] tip on the int4 vocabulary tables,  */
+/* [SIZES] "Tip: int4 Embedding Tables Cost More at Larger Sizes"):         */
+/* embed_tokens, the untied lm_head and the per-layer embeddings are        */
+/* packed int4 in groups of 32, as trained). out[t] = bf16(c * step) of row  */
+/* ids[t] of the table (packed [V][D/2], steps [V][D/32]); a row id outside  */
+/* [0, V) gives a row of zeros. The untied lm_head is the W4A16 GEMM above.  */
+/* ------------------------------------------------------------------------ */
+void qo_embed_q4(const int32_t* ids, int64_t T, const uint8_t* packed, const uint16_t* steps,
+                 int64_t V, int64_t D, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t r = ids[t];
+    for (int64_t k = 0; k < D; ++k)
+      out[t * D + k] = (r < 0 || r >= V)
+                           ? 0
+                           : bf16_nearest(grid_value(packed + r * (D / 2), steps + r * (D / 32), k));
+  }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Mixture-of-experts W4A16 block ([SIZES] "The 4-Bit Builds Stay Slow": the */
 /* 4-bit MoE runs a WNA16 expert path -- bf16 activations, group-32 int4     */
 /* expert weights unpacked to bf16 -- on the fused gate_up / down banks split */

@@ -207,3 +207,14 @@ def moe_bf16_config(E: int | None = None, H: int | None = None, I: int | None = 
     ids, probs = route_topk(logits, topk)
     return dict(E=E, H=H, I=I, T=T, topk=topk, w13_bf16=w13, w2_bf16=w2, x=x, logits=logits,
                 ids=ids, probs=probs)
+
+
+def vocab_config(V: int = 262144, D: int = 1536, T: int = 64, seed: int = 7):
+    """An int4 vocabulary table on the QAT grid (the pages give no table
+    shape: 2^18 rows of 1536 by default) with T token ids uniform in [0, V)
+    and T hidden rows (activations) for the untied lm_head."""
+    rng = np.random.default_rng(seed)
+    codes, steps, w_bf16 = qat_grid(rng, V, D)
+    ids = rng.integers(0, V, size=T, dtype=np.int32)
+    h = activations(rng, T, D)
+    return dict(V=V, D=D, T=T, codes=codes, steps=steps, w_bf16=w_bf16, ids=ids, h=h)
