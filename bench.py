@@ -437,6 +437,54 @@ def c5_rows(q, torch, gen, iters):
     return rows
 
 
+def vocab_rows(q, torch, gen, iters):
+    """int4 vocabulary tables (262144 x 1536): the untied lm_head as a W4A16
+    GEMM with N = 262144 and the embedding lookup, each beside torch on the
+    same table in bf16."""
+    import numpy as np
+
+    rows = {}
+    d = gen.vocab_config()
+    V, D = d["V"], d["D"]
+    w = dev(d["w_bf16"], torch)
+    codes, steps, _ = q.repack_q4_0(w)
+    cps = [(codes, steps)] + [(codes.clone(), steps.clone()) for _ in range(3)]
+    ws = [w, w.clone()]
+    h = dev(d["h"], torch)
+    T = GraphTimer(torch)
+    wb4, wb16 = weight_bytes("w4a16", V, D), weight_bytes("bf16", V, D)
+    for M in (1, 8, 64):
+        xm = h[:M].contiguous()
+        xt = xm.t().contiguous()
+        y = torch.empty(M, V, dtype=torch.bfloat16, device="cuda")
+        t = T.time(lambda i, xm=xm, y=y: q.gemm_w4a16(xm, *cps[i % len(cps)], out=y), reps=16)
+        gbs = wb4 / (t["mean_us"] * 1e3)
+        rows[f"V_lm_head_w4a16_M{M}"] = dict(us=round(t["mean_us"], 2), weight_bytes=wb4,
+                                             GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        best = None
+        for form, fn in (("x@Wt", lambda i, xm=xm: torch.matmul(xm, ws[i % 2].t())),
+                         ("(W@xt)t", lambda i, xt=xt: torch.matmul(ws[i % 2], xt))):
+            tb = T.time(fn, reps=8)
+            if best is None or tb["mean_us"] < best[1]["mean_us"]:
+                best = (form, tb)
+        rows[f"V_lm_head_bf16_torch_M{M}"] = dict(us=round(best[1]["mean_us"], 2), form=best[0],
+                                                  GBps=round(wb16 / (best[1]["mean_us"] * 1e3), 1))
+    for Tn in (64, 8192):
+        ids_np = np.random.default_rng(Tn).integers(0, V, size=Tn, dtype=np.int32)
+        ids = dev(ids_np, torch)
+        ids64 = ids.long()
+        t = T.time(lambda i: q.embed_q4(ids, *cps[i % len(cps)]), reps=16)
+        moved = Tn * (D // 2 + 2 * (D // 32) + 2 * D)
+        rows[f"V_embed_q4_T{Tn}"] = dict(us=round(t["mean_us"], 2), bytes=moved,
+                                         GBps=round(moved / (t["mean_us"] * 1e3), 1))
+        tb = T.time(lambda i: torch.index_select(ws[i % 2], 0, ids64), reps=16)
+        rows[f"V_embed_bf16_torch_T{Tn}"] = dict(us=round(tb["mean_us"], 2))
+    rows["V_table_bytes"] = dict(int4=wb4, bf16=wb16, ratio=round(wb4 / wb16, 4))
+    del cps, ws, codes, steps, w
+    torch.cuda.empty_cache()
+    return rows
+
+
 # ----------------------------------------------------------------------------
 # HBM traffic from hardware counters
 # ----------------------------------------------------------------------------
@@ -619,7 +667,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not a.no_extras:
-        for name, fn in (("C3", c3_rows), ("C4", c4_rows), ("C5", c5_rows)):
+        for name, fn in (("C3", c3_rows), ("C4", c4_rows), ("C5", c5_rows), ("V", vocab_rows)):
             tt = time.time()
             try:
                 rows.update(fn(q, torch, gen, a.kernel_iters))

@@ -143,6 +143,19 @@ int qlin_fp8_fnuz_to_ocp(const uint8_t* w_fnuz, const float* s_in, int64_t N, in
 int qlin_dequant_q4_bf16(const uint8_t* codes, const qlin_bf16* steps, int64_t N, int64_t K,
                          qlin_bf16* out, qlin_stream_t stream);
 
+/* int4 vocabulary table lookup ([E2B] tip on the int4 vocabulary tables;
+ * [SIZES] "Tip: int4 Embedding Tables Cost More at Larger Sizes": the
+ * embedding, untied lm_head and per-layer embedding tables packed int4 in
+ * groups of 32 as trained). out[t][k] = bf16(c * step) of row ids[t] of the
+ * table, the values qlin_dequant_q4_bf16 gives for that row; an id outside
+ * [0, V) yields a row of zeros (ids are device data, so they are not an
+ * error). ids [T] int32 (4-byte aligned); codes [V][D/2] (16-byte aligned),
+ * steps [V][D/32] bf16; out [T][D] bf16 (16-byte aligned); D % 32 == 0,
+ * V <= 2^31 - 1, T * D / 8 < 2^31 (else QLIN_ERR_SHAPE). The untied lm_head
+ * is qlin_gemm_w4a16 with N = V. */
+int qlin_embed_q4(const int32_t* ids, int64_t T, const uint8_t* codes, const qlin_bf16* steps,
+                  int64_t V, int64_t D, qlin_bf16* out, qlin_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Dynamic per-token activation quantisation ([CARD]: activations quantised
  * to FP8 per token at run time; [SIZES] format table: int8 activations per

@@ -46,6 +46,7 @@ _SIGS = {
     "qlin_dequant_q4_bf16": (_INT, [_P, _P, _I64, _I64, _P, _P]),
     "qlin_quant_act": (_INT, [_P, _I64, _I64, _I64, _INT, _P, _P, _P]),
     "qlin_quant_weight": (_INT, [_P, _I64, _I64, _INT, _P, _P, _P]),
+    "qlin_embed_q4": (_INT, [_P, _I64, _P, _P, _I64, _I64, _P, _P]),
     "qlin_fp8_encode_f32": (_INT, [_P, _I64, _INT, _P, _P]),
     "qlin_workspace_bytes": (_SZ, [_INT, _I64, _I64, _I64]),
     "qlin_workspace_init": (_INT, [_P, _SZ, _P]),
@@ -321,6 +322,22 @@ def moe_workspace_layout(T, H, I, E, topk):
     offs = (C.c_size_t * 6)()
     _call("qlin_moe_workspace_layout", T, H, I, E, topk, offs)
     return [int(o) for o in offs]
+
+
+def embed_q4(ids, codes, steps):
+    """Rows ids [T] (int32) of an int4 table (codes u8 [V,D/2], steps bf16
+    [V,D/32]) as bf16 [T,D]; ids outside [0,V) give zero rows."""
+    _check(ids, "ids", torch.int32, 1)
+    _check(codes, "codes", torch.uint8, 2)
+    _check(steps, "steps", torch.bfloat16, 2)
+    V, D2 = codes.shape
+    D = 2 * D2
+    if steps.shape != (V, D // 32):
+        raise ValueError("shape mismatch")
+    out = torch.empty((ids.numel(), D), dtype=torch.bfloat16, device=codes.device)
+    _call("qlin_embed_q4", _ptr(ids), ids.numel(), _ptr(codes), _ptr(steps), V, D, _ptr(out),
+          _stream(codes.device))
+    return out
 
 
 def quant_weight(w: torch.Tensor, fmt="e4m3"):

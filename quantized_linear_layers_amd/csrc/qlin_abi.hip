@@ -130,6 +130,20 @@ int qlin_dequant_q4_bf16(const uint8_t* codes, const qlin_bf16* steps, int64_t N
   return launch_dequant_q4(codes, steps, N, K, out, as_stream(stream));
 }
 
+int qlin_embed_q4(const int32_t* ids, int64_t T, const uint8_t* codes, const qlin_bf16* steps,
+                  int64_t V, int64_t D, qlin_bf16* out, qlin_stream_t stream) {
+  QLIN_CHECK(T >= 0 && V > 0 && D > 0 && D % 32 == 0 && V <= 0x7FFFFFFF && D <= 0x7FFFFFFF &&
+                 T <= 0x7FFFFFFF && T * (D / 8) < ((int64_t)1 << 31),
+             QLIN_ERR_SHAPE);
+  if (T == 0) return QLIN_OK;
+  QLIN_CHECK(ids && codes && steps && out, QLIN_ERR_ARG);
+  QLIN_CHECK(a16(codes) && a16(out) && ((uintptr_t)steps & 1) == 0 && ((uintptr_t)ids & 3) == 0,
+             QLIN_ERR_ALIGN);
+  int rc = device_ok();
+  if (rc) return rc;
+  return launch_embed_q4(ids, T, codes, steps, V, D, out, as_stream(stream));
+}
+
 // ------------------------------------------------------------------ quantisers
 int qlin_quant_act(const qlin_bf16* a, int64_t M, int64_t K, int64_t lda, int fmt, void* a_q,
                    float* a_scale, qlin_stream_t stream) {

@@ -32,6 +32,8 @@ int launch_repack_int8(const uint8_t* codes, const uint16_t* steps, int64_t N, i
                        int8_t* wq, float* ws, hipStream_t st);
 int launch_fnuz_to_ocp(const uint8_t* win, const float* sin, int64_t N, int64_t K, uint8_t* wout,
                        float* sout, int64_t* d_bad, hipStream_t st);
+int launch_embed_q4(const int32_t* ids, int64_t T, const uint8_t* codes, const uint16_t* steps,
+                    int64_t V, int64_t D, uint16_t* out, hipStream_t st);
 int launch_dequant_q4(const uint8_t* codes, const uint16_t* steps, int64_t N, int64_t K,
                       uint16_t* out, hipStream_t st);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t st);

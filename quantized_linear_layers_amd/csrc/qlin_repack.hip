@@ -293,6 +293,41 @@ int launch_dequant_q4(const uint8_t* codes, const uint16_t* steps, int64_t N, in
   return launch_status();
 }
 
+// int4 vocabulary lookup: the dequantiser above on gathered rows. Each wave
+// takes 64 code words (512 values) of one looked-up row, so the row id and
+// the row addresses are wave-uniform (scalar loads and arithmetic); each
+// lane turns one 32-bit code word and its group's step into one 16-byte
+// store, so a wave's loads and stores are contiguous. A row id outside
+// [0, V) writes zeros. cpr = ceil(wpr / 64) waves per row.
+__global__ __launch_bounds__(256) void embed_q4_kernel(const int32_t* __restrict__ ids, uint32_t T,
+                                                       const uint32_t* __restrict__ codes,
+                                                       const uint16_t* __restrict__ steps, int64_t V,
+                                                       uint32_t wpr, uint32_t cpr, uint4* __restrict__ out) {
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4u + (threadIdx.x >> 6));
+  const uint32_t t = wave / cpr;
+  if (t >= T) return;
+  const uint32_t j = (wave - t * cpr) * 64u + (threadIdx.x & 63u);
+  if (j >= wpr) return;
+  const int64_t r = ids[t];
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (r >= 0 && r < V) {
+    const uint32_t cw = __builtin_nontemporal_load(codes + r * wpr + j);
+    const float step = bf16_f32(steps[r * (wpr / 4) + j / 4]);
+    v = __builtin_bit_cast(uint4, dequant8(cw, step, -8.0f * step));
+  }
+  out[(size_t)t * wpr + j] = v;
+}
+
+int launch_embed_q4(const int32_t* ids, int64_t T, const uint8_t* codes, const uint16_t* steps,
+                    int64_t V, int64_t D, uint16_t* out, hipStream_t st) {
+  const uint32_t wpr = (uint32_t)(D / 8), cpr = (wpr + 63) / 64;
+  const uint64_t waves = (uint64_t)T * cpr;
+  embed_q4_kernel<<<dim3((unsigned)((waves + 3) / 4)), 256, 0, st>>>(
+      ids, (uint32_t)T, reinterpret_cast<const uint32_t*>(codes), steps, V, wpr, cpr,
+      reinterpret_cast<uint4*>(out));
+  return launch_status();
+}
+
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* p, size_t n16) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
        i += (size_t)gridDim.x * blockDim.x)

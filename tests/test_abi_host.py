@@ -106,6 +106,12 @@ def test_repack_quant_validation(q):
     assert lib.qlin_quant_weight(A16, 16, 64, 9, A16, A16, None) == q.ERR_ARG
     assert lib.qlin_quant_weight(A_ODD, 16, 64, 1, A16, A16, None) == q.ERR_ALIGN
     assert lib.qlin_quant_weight(A16, 0, 64, 0, A16, A16, None) == q.OK
+    assert lib.qlin_embed_q4(A16, 4, A16, A16, 100, 48, A16, None) == q.ERR_SHAPE  # D % 32
+    assert lib.qlin_embed_q4(A16, 4, A16, A16, 0, 64, A16, None) == q.ERR_SHAPE
+    assert lib.qlin_embed_q4(None, 4, A16, A16, 100, 64, A16, None) == q.ERR_ARG
+    assert lib.qlin_embed_q4(A16, 4, A_ODD, A16, 100, 64, A16, None) == q.ERR_ALIGN
+    assert lib.qlin_embed_q4(A16, 0, A16, A16, 100, 64, A16, None) == q.OK
+    assert lib.qlin_embed_q4(A16, 1 << 20, A16, A16, 100, 1 << 14, A16, None) == q.ERR_SHAPE
 
 
 def test_moe_validation(q):

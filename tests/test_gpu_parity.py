@@ -640,3 +640,56 @@ def test_moe_swiglu_oai_c5(q, oracle, c5_online, T):
     dd["x"], dd["ids"], dd["probs"] = d["x"][:T], d["ids"][:T], d["probs"][:T]
     tokens = None if T == 64 else np.arange(0, T, 16)
     _moe_check(q, oracle, dd, w, tokens=tokens, act=(ALPHA, BETA, 7.0))
+
+
+# ------------------------------------------------------ int4 vocabulary tables
+def _vocab(oracle, **kw):
+    d = gen.vocab_config(**kw)
+    d["packed"], d["steps_bits"], _ = oracle.repack_q4_0(d["w_bf16"])
+    return d
+
+
+@pytest.mark.parametrize("V,D,T", [(5000, 1536, 300), (700, 8960, 64), (33, 32, 5)])
+def test_embed_q4_bitexact(q, oracle, V, D, T):
+    """Every value of the looked-up rows, with repeated ids and ids outside
+    the table (zero rows); D = 8960 is a per-layer embedding width."""
+    d = _vocab(oracle, V=V, D=D, T=T, seed=V + D)
+    ids = d["ids"].copy()
+    ids[0] = -1
+    ids[-1] = V
+    ids[1] = ids[2]
+    ref = oracle.embed_q4(ids, d["packed"], d["steps_bits"])
+    g = host(q.embed_q4(dev(ids), dev(d["packed"]), dev(d["steps_bits"])))
+    assert np.array_equal(g, ref)
+    assert not g[[0, -1]].any()
+
+
+@pytest.fixture(scope="module")
+def vocab_full(oracle):
+    return _vocab(oracle)
+
+
+@pytest.mark.parametrize("T", [64, 8192])
+def test_embed_q4_full_table(q, oracle, vocab_full, T):
+    d = vocab_full
+    ids = np.random.default_rng(T).integers(0, d["V"], size=T, dtype=np.int32)
+    ref = oracle.embed_q4(ids, d["packed"], d["steps_bits"])
+    g = host(q.embed_q4(dev(ids), dev(d["packed"]), dev(d["steps_bits"])))
+    assert np.array_equal(g, ref)
+
+
+def test_lm_head_w4a16_full_table_sampled(q, oracle, vocab_full):
+    """The untied lm_head: logits [M, V] = h . table^T through the W4A16
+    GEMM at N = 262144, sampled against the oracle, plus the bf16 output
+    equal to the RNE of the fp32 output."""
+    d = vocab_full
+    pk, st = dev(d["packed"]), dev(d["steps_bits"])
+    rng = np.random.default_rng(23)
+    for M in (1, 8, 64):
+        a = dev(d["h"][:M])
+        g = host(q.gemm_w4a16(a, pk, st, out_dtype=torch.float32))
+        g16 = host(q.gemm_w4a16(a, pk, st))
+        mi, ni = _sampled(rng, M, d["V"], 3000)
+        ref = oracle.gemm_w4a16_sample(d["h"][:M], d["packed"], d["steps_bits"], mi, ni)
+        tol_check(g[mi, ni], ref, f"lm_head M={M}", rms=float(np.sqrt(np.mean(ref.astype(np.float64) ** 2))))
+        assert np.array_equal(g16, gen.to_bf16_bits(g))
