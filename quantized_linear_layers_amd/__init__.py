@@ -290,7 +290,7 @@ def gemm_w4a16(a, codes, steps, out_dtype=torch.bfloat16, out=None):
     return y
 
 
-def _linear(name, op, x, w_q, w_scale, wdtype):
+def _linear(name, op, x, w_q, w_scale, wdtype, out=None):
     if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2
             and x.stride(1) == 1):
         raise ValueError("x must be a 2-D bf16 device tensor with unit column stride")
@@ -300,21 +300,27 @@ def _linear(name, op, x, w_q, w_scale, wdtype):
     N = w_q.shape[0]
     if w_q.shape[1] != K or w_scale.numel() != N:
         raise ValueError("shape mismatch")
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if out is not None:
+        _check(out, "out", torch.bfloat16, 2)
+        if out.shape != (M, N):
+            raise ValueError("out shape mismatch")
+        y = out
+    else:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     ws = workspace(workspace_bytes(op, M, N, K), x.device)
     _call(name, _ptr(x), x.stride(0), _ptr(w_q), _ptr(w_scale), M, N, K, _ptr(y), _ptr(ws),
           ws.numel(), _stream(x.device))
     return y
 
 
-def linear_fp8(x, w_q, w_scale):
+def linear_fp8(x, w_q, w_scale, out=None):
     """Per-token FP8 quantisation of x followed by the FP8 GEMM (bf16 out)."""
-    return _linear("qlin_linear_fp8", OP_LINEAR_FP8, x, w_q, w_scale, torch.uint8)
+    return _linear("qlin_linear_fp8", OP_LINEAR_FP8, x, w_q, w_scale, torch.uint8, out)
 
 
-def linear_w8a8(x, w_q, w_scale):
+def linear_w8a8(x, w_q, w_scale, out=None):
     """Per-token int8 quantisation of x followed by the int8 GEMM."""
-    return _linear("qlin_linear_w8a8", OP_LINEAR_W8A8, x, w_q, w_scale, torch.int8)
+    return _linear("qlin_linear_w8a8", OP_LINEAR_W8A8, x, w_q, w_scale, torch.int8, out)
 
 
 # ---------------------------------------------------------------- MoE

@@ -693,3 +693,36 @@ def test_lm_head_w4a16_full_table_sampled(q, oracle, vocab_full):
         ref = oracle.gemm_w4a16_sample(d["h"][:M], d["packed"], d["steps_bits"], mi, ni)
         tol_check(g[mi, ni], ref, f"lm_head M={M}", rms=float(np.sqrt(np.mean(ref.astype(np.float64) ** 2))))
         assert np.array_equal(g16, gen.to_bf16_bits(g))
+
+
+# ------------------------------------------ linear = quantiser + GEMM
+# (N, K, M list): C2 decode layer; ragged K; a split-K grid (8 column tiles);
+# K past 16384 (the quantiser's two-pass rows); C3 layer
+LINEAR_CASES = [(8192, 2048, (1, 5, 8, 16)), (512, 80, (1, 3, 16)), (512, 2048, (1, 16)),
+                (1024, 16400, (2,)), (25600, 5120, (8,))]
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("case", LINEAR_CASES, ids=[f"N{c[0]}_K{c[1]}" for c in LINEAR_CASES])
+def test_linear_equals_quant_then_gemm(q, fmt, case):
+    """The linear entry point (per-token quantisation into its workspace,
+    then the GEMM) equals the two calls made separately, bit for bit; strided
+    activation rows and a zero row included."""
+    N, K, Ms = case
+    rng = np.random.default_rng(N + K)
+    wq, ws = q.quant_weight(dev(gen.dense_bf16(rng, N, K)), "int8" if fmt == "int8" else "e4m3")
+    xf = gen.activations(rng, max(Ms), K + 8)
+    if max(Ms) > 1:
+        xf[1] = 0
+    xd = dev(xf)
+    for M in Ms:
+        x = xd[:M, :K]
+        if fmt == "fp8":
+            y1 = q.linear_fp8(x, wq, ws)
+            y2 = q.gemm_fp8(*q.quant_act(x, "e4m3"), wq, ws)
+        else:
+            y1 = q.linear_w8a8(x, wq, ws)
+            y2 = q.gemm_w8a8(*q.quant_act(x, "int8"), wq, ws)
+        assert np.array_equal(host(y1), host(y2)), f"{fmt} N={N} K={K} M={M}"
+        if M > 1:
+            assert not host(y1)[1].any()
