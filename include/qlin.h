@@ -189,7 +189,9 @@ int qlin_fp8_encode_f32(const float* x, int64_t n, int fmt, uint8_t* out, qlin_s
  * call that uses the workspace (allocate it zeroed, or call
  * qlin_workspace_init); every call leaves it zero again, whatever its shape,
  * so one zeroed workspace serves all later calls. Calls that share one
- * workspace must be ordered on one stream.
+ * workspace must be ordered on one stream. The MoE calls overwrite their
+ * whole workspace: a buffer lent to them must be zeroed again
+ * (qlin_workspace_init) before it serves a GEMM.
  * ------------------------------------------------------------------------ */
 size_t qlin_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 

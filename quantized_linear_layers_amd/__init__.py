@@ -133,6 +133,21 @@ def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
     return ws
 
 
+_scratch_cache: dict[int, torch.Tensor] = {}
+
+
+def scratch(nbytes: int, device: torch.device) -> torch.Tensor:
+    """Per-device scratch of at least nbytes for calls that overwrite their
+    whole workspace (the MoE blocks). Kept apart from `workspace`, whose
+    counter area the split-K GEMMs need to find zero."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _scratch_cache.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _scratch_cache[idx] = ws
+    return ws
+
+
 def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
     return int(_lib.qlin_workspace_bytes(op, M, N, K))
 
@@ -377,7 +392,7 @@ def moe_fp8(x, topk_ids, topk_w, w13, s13, w2, s2, return_stages=False, swiglu_o
             topk_w.shape != topk_ids.shape or topk_ids.shape[0] != T:
         raise ValueError("shape mismatch")
     nb = int(_lib.qlin_moe_workspace_bytes(T, H, I, E, topk))
-    ws = workspace(nb, x.device) if not return_stages else \
+    ws = scratch(nb, x.device) if not return_stages else \
         torch.empty(max(nb, 256), dtype=torch.uint8, device=x.device)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     if swiglu_oai is None:
@@ -422,7 +437,7 @@ def moe_w4a16(x, topk_ids, topk_w, codes13, steps13, codes2, steps2, return_stag
             steps2.shape != (E, H, I // 32) or topk_w.shape != topk_ids.shape or topk_ids.shape[0] != T:
         raise ValueError("shape mismatch")
     nb = int(_lib.qlin_moe_w4a16_workspace_bytes(T, H, I, E, topk))
-    ws = workspace(nb, x.device) if not return_stages else \
+    ws = scratch(nb, x.device) if not return_stages else \
         torch.empty(max(nb, 256), dtype=torch.uint8, device=x.device)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
     _call("qlin_moe_w4a16", _ptr(x), T, H, I, E, topk, _ptr(topk_ids), _ptr(topk_w), _ptr(codes13),

@@ -726,3 +726,22 @@ def test_linear_equals_quant_then_gemm(q, fmt, case):
         assert np.array_equal(host(y1), host(y2)), f"{fmt} N={N} K={K} M={M}"
         if M > 1:
             assert not host(y1)[1].any()
+
+
+def test_split_k_gemm_after_moe(q, oracle):
+    """Regression: a MoE call (which overwrites its whole workspace) followed
+    by a split-K GEMM (which needs its workspace's counter area zero) gives
+    the correct GEMM result: the two take separate buffers."""
+    d = gen.moe_config(E=8, H=256, I=128, T=24, topk=2, seed=13)
+    w = [dev(a) for a in _moe_weights(oracle, d)]
+    q.moe_fp8(dev(d["x"]), dev(d["ids"]), dev(d["probs"]), *w)
+    N, K = 512, 2048  # 16 column tiles: split over K
+    rng = np.random.default_rng(3)
+    wq, ws = oracle.quant_weight(gen.dense_bf16(rng, N, K), 0)
+    x = gen.activations(rng, 1, K)
+    aq, sa = oracle.quant_act(x, 0)
+    y32, _ = oracle.gemm_fp8(aq, sa, wq, ws)
+    g = host(q.gemm_fp8(dev(aq), dev(sa), dev(wq), dev(ws), out_dtype=torch.float32))
+    tol_check(g, y32, "split-K fp8 after MoE")
+    y1 = host(q.linear_fp8(dev(x), dev(wq), dev(ws)))
+    assert np.array_equal(y1, gen.to_bf16_bits(g))
