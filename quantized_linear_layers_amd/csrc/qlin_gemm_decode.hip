@@ -285,7 +285,11 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   const int64_t cus = decode_cus();
   c.MB = (int)((M + 15) / 16);
   c.NB = (kind != kGemmW4 || c.MB >= 3) && (N + 127) / 128 >= 3 * cus / 4 ? 2 : 1;
-  c.NW = kind == kGemmW4 && c.NB == 2 ? 8 : 4;
+  // fp8/int8 at M <= 16 with one block per wave: 2 waves per workgroup, so
+  // the same waves spread over twice the CUs (K=2048, N=8192: M = 1 5.5 ->
+  // 5.3 us, M = 8 6.1 -> 5.7 us; 1 wave per workgroup was slower, and at
+  // M = 64 2 waves gained nothing)
+  c.NW = kind == kGemmW4 && c.NB == 2 ? 8 : kind != kGemmW4 && c.MB == 1 && c.NB == 1 ? 2 : 4;
   // W4A16 at M <= 16 on a layer too narrow for the column tiles to fill the
   // device: the 4 waves of a workgroup split K instead of the grid (one
   // block each; K=2048, N=8192, M = 1: 5.9 instead of 6.9 us with 2 global
@@ -321,7 +325,7 @@ static auto with_decode_inst(int kind, int MB, int NB, bool wk, bool sb, F&& f) 
     case 1:                                                                                  \
       if constexpr (K == kGemmW4) if (wk) return f.template operator()<K, 1, 1, D1, SB, 4, true>(); \
       if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 1, 2, D2, SB, 4, false>(); \
-      return f.template operator()<K, 1, 1, D1, SB, 4, false>();                             \
+      return f.template operator()<K, 1, 1, D1, SB, K == kGemmW4 ? 4 : 2, false>();          \
     case 2:                                                                                  \
       if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 2, 2, D2, SB, 4, false>(); \
       return f.template operator()<K, 2, 1, D2, SB, 4, false>();                             \
