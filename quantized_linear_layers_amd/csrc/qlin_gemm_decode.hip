@@ -302,7 +302,6 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   const int64_t want = kind != kGemmW4 ? cus / 2 : c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
   int64_t S = (want + c.tiles - 1) / c.tiles;
   S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
-  if (const char* e = getenv("QLIN_DECODE_SPLIT")) S = std::max(1, atoi(e));  // tuning override
   if (c.tiles > (int)(kGemmCounterBytes / 4)) S = 1;  // one counter per tile; such grids need no split
   int64_t steps_per = (ksteps + S - 1) / S;
   steps_per = (steps_per + 1) / 2 * 2;  // whole 256-K chunks
