@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--kernel-iters", type=int, default=64,
                     help="event-timed launches per kernel for the per-kernel rows")
+    ap.add_argument("--pmc-workload", choices=("prefill", "moe"), default=None,
+                    help="counter-collection workload for rocprofv3 --pmc: the C4 prefill GEMMs "
+                         "(fp8, int8, W4A16, torch bf16; 3 launches each) or the C5 MoE blocks "
+                         "(fp8, fp8 + SwiGLU-OAI, W4A16 at T = 64 and 512; 3 launches each), "
+                         "then the 256 MiB copy that calibrates FETCH_SIZE / WRITE_SIZE")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="counter-collection workload: every decode GEMM of the step, 8 eager "
                          "launches each, then a 256 MiB device copy (the counters' calibration); "
@@ -527,6 +532,70 @@ def pmc_pass(q, torch, L, x, Ms, bufs, launches=8):
                       "sources_sha256": decode_sources_sha256()}), flush=True)
 
 
+def pmc_workload(q, torch, which, launches=3):
+    """Counter-collection workloads beyond the decode step (run under
+    rocprofv3 --pmc): synthetic operands of the C4 / C5 shapes built on the
+    device (uniform random codes, bf16 steps in [0.001, 0.021], N(0,1)
+    activations, N(0, 0.02) bf16 weights quantised per channel), each call
+    launched `launches` times in a fixed order, then the calibration copy."""
+    torch.manual_seed(0)
+    order = []
+
+    def rep(name, fn):
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            fn()
+        torch.cuda.synchronize()
+        order.append(name)
+
+    if which == "prefill":
+        M = 8192
+        for K, N in ((4096, 14336), (14336, 4096)):
+            a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+            w = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+            aq, sa = q.quant_act(a, "e4m3")
+            ai, sai = q.quant_act(a, "int8")
+            wq, ws = q.quant_weight(w, "e4m3")
+            wi, wsi = q.quant_weight(w, "int8")
+            codes = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda")
+            steps = (torch.rand(N, K // 32, device="cuda") * 0.02 + 0.001).to(torch.bfloat16)
+            tag = f"C4_K{K}_N{N}"
+            rep(f"{tag}_fp8", lambda: q.gemm_fp8(aq, sa, wq, ws))
+            rep(f"{tag}_int8", lambda: q.gemm_w8a8(ai, sai, wi, wsi))
+            rep(f"{tag}_w4a16", lambda: q.gemm_w4a16(a, codes, steps))
+            rep(f"{tag}_bf16_torch", lambda: torch.matmul(a, w.t()))
+            del a, w, aq, ai, wq, wi, codes, steps
+    else:
+        import numpy as np
+
+        import gen
+        E, H, I, topk = 128, 2048, 768, 8
+        w13, s13 = q.quant_weight((torch.randn(E * 2 * I, H, device="cuda") * 0.02).to(torch.bfloat16))
+        w2, s2 = q.quant_weight((torch.randn(E * H, I, device="cuda") * 0.02).to(torch.bfloat16))
+        fp8w = (w13.view(E, 2 * I, H), s13.view(E, 2 * I), w2.view(E, H, I), s2.view(E, H))
+        w4 = (torch.randint(0, 256, (E, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
+              (torch.rand(E, 2 * I, H // 32, device="cuda") * 0.02 + 0.001).to(torch.bfloat16),
+              torch.randint(0, 256, (E, H, I // 2), dtype=torch.uint8, device="cuda"),
+              (torch.rand(E, H, I // 32, device="cuda") * 0.02 + 0.001).to(torch.bfloat16))
+        rng = np.random.default_rng(0)
+        for T in (64, 512):
+            ids, pr = gen.route_topk(rng.standard_normal((T, E), dtype=np.float32), topk)
+            ids, pr = dev(ids, torch), dev(pr, torch)
+            x = torch.randn(T, H, device="cuda").to(torch.bfloat16)
+            rep(f"C5_moe_fp8_T{T}", lambda: q.moe_fp8(x, ids, pr, *fp8w))
+            rep(f"C5_moe_fp8_swiglu_oai_T{T}", lambda: q.moe_fp8(x, ids, pr, *fp8w, swiglu_oai=(1.702, 1.0, 7.0)))
+            rep(f"C5_moe_w4a16_T{T}", lambda: q.moe_w4a16(x, ids, pr, *w4))
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_workload": which, "order": order, "launches": launches, "copy_bytes": n,
+                      "copies": 4}), flush=True)
+
+
 def traffic_table():
     """Per-launch HBM bytes of each decode GEMM of the step, from the
     committed counter summary, if it was taken on the current kernel sources
@@ -595,6 +664,9 @@ def main():
 
     torch.cuda.set_device(0)
     t_start = time.time()
+    if a.pmc_workload:
+        pmc_workload(q, torch, a.pmc_workload)
+        return
     cfg = gen.CONFIGS[2]
     d = gen.linear_config(2)
     N, K, Ms = d["N"], d["K"], cfg["M"]
