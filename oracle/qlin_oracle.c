@@ -27,7 +27,7 @@
  * E4M3 round-to-nearest-even with saturation; statistics in fp64.
  * Build: gcc -O2 -fopenmp -ffp-contract=off (no fast-math).
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - int4 codes are signed [-8,7], stored offset-binary u = c + 8, two per
  *     byte, low nibble = even k; one bf16 step per (row, 32 values).
  *   - q4_0 step recovery keeps the smallest step that reproduces every
