@@ -52,7 +52,8 @@ def test_fp8_encoder_dense_sweep(q, oracle, fmt):
 
 # ------------------------------------------------------------------ quantisers
 @pytest.mark.parametrize("fmt", ["e4m3", "int8", "e4m3fnuz"])
-@pytest.mark.parametrize("case", ["c1", "c2", "c3", "ragged", "zero_rows", "long"])
+@pytest.mark.parametrize("case", ["c1", "c2", "c3", "ragged", "zero_rows", "long", "tall_k80", "tall_k768",
+                                  "tall_k2048"])
 def test_quant_act_bit_exact(q, oracle, fmt, case):
     if case == "c1":
         a = gen.linear_config(1)["a"]
@@ -67,8 +68,15 @@ def test_quant_act_bit_exact(q, oracle, fmt, case):
         a[1] = 0
         a[4] = 0
         a[4, 7] = gen.to_bf16_bits(np.float32([-3e-30]))[0]
-    else:
+    elif case == "long":
         a = gen.linear_config(1, n=16, k=20480, m=3)["a"]  # rows beyond 16384: two-pass path
+    else:
+        # >= 1024 rows of <= 2048 elements: one wave per row (ragged row count
+        # against the four rows of a workgroup, zero rows included)
+        K = int(case[6:])
+        a = gen.activations(np.random.default_rng(K), 1027 if K != 2048 else 1024, K).copy()
+        a[5] = 0
+        a[-1] = 0
     f = {"e4m3": OCP, "int8": INT8, "e4m3fnuz": FNUZ}[fmt]
     qg, sg = q.quant_act(dev(a), fmt)
     qo, so = oracle.quant_act(a, f)
