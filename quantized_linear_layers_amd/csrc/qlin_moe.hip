@@ -292,15 +292,28 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   if (i >= (long long)T * hq) return;
   const int t = (int)(i / hq), h = (int)(i % hq) * 4;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-  for (int j = 0; j < topk; ++j) {
-    const int e = ids[t * topk + j];
-    const float w = (e >= 0 && e < E) ? wts[t * topk + j] : 0.0f;
-    const float4 v = *reinterpret_cast<const float4*>(d + ((size_t)t * topk + j) * H + h);
-    if (e >= 0 && e < E) {
-      a0 = a0 + w * v.x;
-      a1 = a1 + w * v.y;
-      a2 = a2 + w * v.z;
-      a3 = a3 + w * v.w;
+  // slots in batches of 8: every load of a batch is issued before the first
+  // sum (clamped slot indices, no branch between the loads), then the sums
+  // run in slot order
+  for (int j0 = 0; j0 < topk; j0 += 8) {
+    int ev[8];
+    float wv[8];
+    float4 dv[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int j = min(j0 + b, topk - 1);
+      ev[b] = ids[t * topk + j];
+      wv[b] = wts[t * topk + j];
+      dv[b] = *reinterpret_cast<const float4*>(d + ((size_t)t * topk + j) * H + h);
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (j0 + b < topk && ev[b] >= 0 && ev[b] < E) {
+        a0 = a0 + wv[b] * dv[b].x;
+        a1 = a1 + wv[b] * dv[b].y;
+        a2 = a2 + wv[b] * dv[b].z;
+        a3 = a3 + wv[b] * dv[b].w;
+      }
     }
   }
   const uint32_t lo = f32_bf16_rne(a0) | (f32_bf16_rne(a1) << 16);
