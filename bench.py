@@ -288,6 +288,30 @@ def bf16_rows(torch, L, x, Ms, iters, tag):
 # ----------------------------------------------------------------------------
 # extras
 # ----------------------------------------------------------------------------
+def repack_fidelity(torch, codes, steps, wq, ws, fmt, rows_per=2048):
+    """Fidelity of an FP8 repack against the QAT grid values it came from:
+    relative RMS error sqrt(sum (dec(q)*s - w)^2 / sum w^2) and the largest
+    per-row max error over the row's max |w| (w = c*step, exact), in fp64
+    with torch on the device, a block of rows at a time."""
+    f8 = torch.float8_e4m3fn if fmt == "e4m3" else torch.float8_e4m3fnuz
+    num = den = 0.0
+    mx = 0.0
+    N = codes.shape[0]
+    for n0 in range(0, N, rows_per):
+        c = codes[n0:n0 + rows_per].to(torch.int32)
+        grid = torch.stack(((c & 15) - 8, (c >> 4) - 8), dim=-1).reshape(c.shape[0], -1).to(torch.float64)
+        st = steps[n0:n0 + rows_per].to(torch.float64).repeat_interleave(32, dim=1)
+        w = grid * st
+        d = wq[n0:n0 + rows_per].view(f8).to(torch.float64) * ws[n0:n0 + rows_per].to(torch.float64)[:, None]
+        e = d - w
+        num += float((e * e).sum())
+        den += float((w * w).sum())
+        amax = w.abs().amax(dim=1)
+        r = torch.where(amax > 0, e.abs().amax(dim=1) / amax, torch.zeros_like(amax))
+        mx = max(mx, float(r.max()))
+    return (num / den) ** 0.5 if den > 0 else 0.0, mx
+
+
 def c3_rows(q, torch, gen, iters):
     d = gen.linear_config(3)
     copies = max(2, int(math.ceil(1.1 * GIB / weight_bytes("fp8", d["N"], d["K"]))))
@@ -306,6 +330,12 @@ def c3_rows(q, torch, gen, iters):
     codes, steps = L.w4[0]
     t = T.time(lambda i: q.repack_fp8(codes, steps), 8, filler_ms=5)
     rows["C3_repack_fp8"] = dict(us=round(t["mean_us"], 1))
+    for fmt in ("e4m3", "e4m3fnuz"):
+        wq_, ws_ = q.repack_fp8(codes, steps, fmt)
+        rr, mr = repack_fidelity(torch, codes, steps, wq_, ws_, fmt)
+        rows["C3_repack_fp8"][f"rel_rms_{fmt}"] = round(rr, 6)
+        rows["C3_repack_fp8"][f"max_err_over_row_max_{fmt}"] = round(mr, 6)
+        del wq_, ws_
     wf, sf = q.repack_fp8(codes, steps, "e4m3fnuz")
     wo, so, bad = q.fp8_fnuz_to_ocp(wf, sf)
     t = T.time(lambda i: q.fp8_fnuz_to_ocp(wf, sf), 8, filler_ms=5)
