@@ -753,3 +753,17 @@ def test_split_k_gemm_after_moe(q, oracle):
     tol_check(g, y32, "split-K fp8 after MoE")
     y1 = host(q.linear_fp8(dev(x), dev(wq), dev(ws)))
     assert np.array_equal(y1, gen.to_bf16_bits(g))
+
+
+def test_moe_degenerate_shapes(q, oracle):
+    """One expert, one token, top-1 (FP8 and W4A16 blocks), and a W4A16
+    batch whose every slot names an expert outside [0, E): an exactly zero
+    output."""
+    d = gen.moe_config(E=1, H=64, I=32, T=1, topk=1, seed=71)
+    _moe_check(q, oracle, d, _moe_weights(oracle, d))
+    _moe_w4_check(q, oracle, d, _moe_w4_weights(oracle, d))
+    d = gen.moe_config(E=4, H=64, I=32, T=3, topk=2, seed=72)
+    w = _moe_w4_weights(oracle, d)
+    ids = np.int32([[-1, 4], [7, -2], [1 << 30, -1]])
+    y = host(q.moe_w4a16(dev(d["x"]), dev(ids), dev(d["probs"]), *[dev(a) for a in w]))
+    assert not y.any()
