@@ -767,3 +767,18 @@ def test_moe_degenerate_shapes(q, oracle):
     ids = np.int32([[-1, 4], [7, -2], [1 << 30, -1]])
     y = host(q.moe_w4a16(dev(d["x"]), dev(ids), dev(d["probs"]), *[dev(a) for a in w]))
     assert not y.any()
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8", "w4a16"])
+def test_gemm_smallest_shapes(q, oracle, fmt):
+    """N = 16 and K = 32 (one int4 group; the weights of every format come
+    from the QAT grid): most lanes of every tile hold clamped rows and
+    columns; decode (M = 1, 17) and prefill (M = 65) paths."""
+    K = 32
+    d = gen.linear_config(1, n=16, k=K, m=65)
+    ops = _operands(oracle, d, fmt)
+    for M in (1, 17, 65):
+        y32, y16 = _oracle_gemm(oracle, fmt, ops, M)
+        g32 = host(_gpu_gemm(q, fmt, ops, M, torch.float32))
+        g16 = host(_gpu_gemm(q, fmt, ops, M, torch.bfloat16))
+        _compare(fmt, g32, g16, y32, y16, f"{fmt} N=16 K={K} M={M}")
