@@ -782,3 +782,16 @@ def test_gemm_smallest_shapes(q, oracle, fmt):
         g32 = host(_gpu_gemm(q, fmt, ops, M, torch.float32))
         g16 = host(_gpu_gemm(q, fmt, ops, M, torch.bfloat16))
         _compare(fmt, g32, g16, y32, y16, f"{fmt} N=16 K={K} M={M}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8", "w4a16"])
+def test_gemm_longest_k(q, oracle, fmt):
+    """K = 131072, near the entry points' K limit (133144): the decode path
+    splits it 8 ways (M = 1), the prefill path walks it in one tile (M = 65)."""
+    d = gen.linear_config(1, n=32, k=131072, m=65)
+    ops = _operands(oracle, d, fmt)
+    for M in (1, 65):
+        y32, y16 = _oracle_gemm(oracle, fmt, ops, M)
+        g32 = host(_gpu_gemm(q, fmt, ops, M, torch.float32))
+        g16 = host(_gpu_gemm(q, fmt, ops, M, torch.bfloat16))
+        _compare(fmt, g32, g16, y32, y16, f"{fmt} N=32 K=131072 M={M}")
