@@ -795,3 +795,52 @@ def test_gemm_longest_k(q, oracle, fmt):
         g32 = host(_gpu_gemm(q, fmt, ops, M, torch.float32))
         g16 = host(_gpu_gemm(q, fmt, ops, M, torch.bfloat16))
         _compare(fmt, g32, g16, y32, y16, f"{fmt} N=32 K=131072 M={M}")
+
+
+def test_graph_replay_matches_eager(q, oracle):
+    """A captured HIP graph of a split-K W4A16 GEMM (M = 64, 16 column
+    tiles, 4 K splits), an FP8 linear (M = 8) and a W4A16 MoE block, replayed
+    three times with eager calls of other shapes in between: every replay
+    equals the eager result bit for bit (the split-K counters are back at
+    zero after each call; nothing in the library records a memset)."""
+    d = gen.linear_config(2, n=1024, k=2048, m=64)
+    ops4 = _operands(oracle, d, "w4a16")
+    ops8 = _operands(oracle, d, "fp8")
+    a = dev(d["a"])
+    pk, st = dev(ops4["packed"]), dev(ops4["steps"])
+    wq, ws = dev(ops8["wq"]), dev(ops8["ws"])
+    dm = gen.moe_config(E=8, H=256, I=128, T=24, topk=2, seed=13)
+    wm = [dev(x) for x in _moe_w4_weights(oracle, dm)]
+    xm, ids, pr = dev(dm["x"]), dev(dm["ids"]), dev(dm["probs"])
+    y4 = torch.empty(64, 1024, dtype=torch.bfloat16, device="cuda")
+    y8 = torch.empty(8, 1024, dtype=torch.bfloat16, device="cuda")
+    ym = torch.empty(24, 256, dtype=torch.bfloat16, device="cuda")
+
+    def calls():
+        q.gemm_w4a16(a, pk, st, out=y4)
+        q.linear_fp8(a[:8], wq, ws, out=y8)
+        ym.copy_(q.moe_w4a16(xm, ids, pr, *wm))
+
+    calls()
+    torch.cuda.synchronize()
+    ref = [host(y4), host(y8), host(ym)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(3):
+        for y in (y4, y8, ym):
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y4), ref[0]) and np.array_equal(host(y8), ref[1]) and \
+            np.array_equal(host(ym), ref[2]), f"replay {rep}"
+        # eager work of other shapes between replays (another split-K grid)
+        q.gemm_w4a16(a[:40], pk, st)
+        q.linear_fp8(a[:3], wq, ws)
+        torch.cuda.synchronize()
