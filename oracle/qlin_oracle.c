@@ -187,6 +187,20 @@ static int step_reproduces(const uint16_t* w, float step, int8_t* c) {
   return 1;
 }
 
+/* Number of stored values that the nearest codes on `step`, clamped to
+ * [-8, 7], reproduce (0 for a step that is not finite and positive). */
+static int step_count(const uint16_t* w, float step) {
+  if (!(step > 0.0f) || !isfinite(step)) return 0;
+  int n = 0;
+  for (int j = 0; j < 32; ++j) {
+    float q = rintf(bf16_value(w[j]) / step);
+    if (q < -8.0f) q = -8.0f;
+    if (q > 7.0f) q = 7.0f;
+    n += bf16_nearest(q * step) == w[j];
+  }
+  return n;
+}
+
 /* Returns 1 if the group was recovered unambiguously, 0 if it is counted.
  * Writes codes (32) and the bf16 step. */
 static int recover_group(const uint16_t* w, int8_t* codes, uint16_t* step_out) {
@@ -231,8 +245,31 @@ static int recover_group(const uint16_t* w, int8_t* codes, uint16_t* step_out) {
     }
   }
   if (!isfinite(best)) {
-    /* Not on any 4-bit grid: nearest codes on step bf16(amax / 7). */
-    best = bf16_value(bf16_nearest(amax / 7.0f));
+    /* No bf16 step puts the whole group on a 4-bit grid (a trained step that
+     * is not a bf16 value does this: bf16(c * step) rounds c * step for some
+     * codes). Keep the candidate step -- |w_i| / p and the neighbours above --
+     * whose nearest codes reproduce the most stored values, the smaller step
+     * on ties; codes are nearest on it, clamped to [-8, 7]. */
+    int most = -1;
+    for (int i = 0; i < 32; ++i) {
+      float a = fabsf(bf16_value(w[i]));
+      if (a == 0.0f) continue;
+      for (int p = 0; p < 4; ++p) {
+        float s = a / P[p];
+        int n = step_count(w, s);
+        if (n > most || (n == most && s < best)) { most = n; best = s; }
+      }
+    }
+    static const float A[4] = {3.0f, 5.0f, 6.0f, 7.0f};
+    for (int ai = 0; ai < 4; ++ai) {
+      uint16_t c0 = bf16_nearest(amax / A[ai]);
+      for (int d = -8; d <= 8; ++d) {
+        float s = bf16_value((uint16_t)(c0 + d));
+        if (!(s > 0.0f) || !isfinite(s)) continue;
+        int n = step_count(w, s);
+        if (n > most || (n == most && s < best)) { most = n; best = s; }
+      }
+    }
     for (int j = 0; j < 32; ++j) {
       float q = rintf(bf16_value(w[j]) / best);
       if (q < -8.0f) q = -8.0f;

@@ -50,16 +50,20 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # element generators
 # --------------------------------------------------------------------------
-def qat_grid(rng: np.random.Generator, n: int, k: int):
+def qat_grid(rng: np.random.Generator, n: int, k: int, bf16_steps: bool = True):
     """One Linear weight on the QAT q4_0 grid.
 
     Returns (codes int8 [n,k] in [-8,7], steps float32 [n,k/32] holding bf16
-    values, w_bf16 uint16 [n,k] = bf16(code*step)).
+    values, w_bf16 uint16 [n,k] = bf16(code*step)). With bf16_steps=False the
+    steps keep their full fp32 draw (a trained checkpoint's steps need not be
+    bf16 values), so bf16(code*step) rounds values whose product needs more
+    than bf16's 8 significant bits.
     """
     assert k % GROUP == 0
     codes = rng.integers(-8, 8, size=(n, k), dtype=np.int8)
     steps = rng.lognormal(np.log(0.01), 0.5, size=(n, k // GROUP)).astype(np.float32)
-    steps = bf16_bits_to_f32(to_bf16_bits(steps))
+    if bf16_steps:
+        steps = bf16_bits_to_f32(to_bf16_bits(steps))
     w = codes.astype(np.float32).reshape(n, k // GROUP, GROUP) * steps[:, :, None]
     w_bf16 = to_bf16_bits(w.reshape(n, k))
     return codes, steps, w_bf16
@@ -114,18 +118,20 @@ CONFIGS = {
 }
 
 
-def linear_config(cfg: int, n: int | None = None, k: int | None = None, m: int | None = None):
+def linear_config(cfg: int, n: int | None = None, k: int | None = None, m: int | None = None,
+                  bf16_steps: bool = True):
     """Inputs of a dense configuration (1, 2 or 3).
 
     Optional n/k/m override the sizes (same seed and draw order), for small
-    parity cases of the same distribution.
+    parity cases of the same distribution. bf16_steps=False draws the same
+    grid with unrounded fp32 steps (see qat_grid).
     """
     c = CONFIGS[cfg]
     rng = np.random.default_rng(c["seed"])
     N = c["N"] if n is None else n
     K = c["K"] if k is None else k
     M = max(c["M"]) if m is None else m
-    codes, steps, w_bf16 = qat_grid(rng, N, K)
+    codes, steps, w_bf16 = qat_grid(rng, N, K, bf16_steps)
     a = activations(rng, M, K)
     return dict(codes=codes, steps=steps, w_bf16=w_bf16, a=a, M=M, N=N, K=K)
 
