@@ -96,12 +96,15 @@ int qlin_last_hip_error(void);
  *   codes    [N][K/2] output, offset-binary u = c + 8, two per byte, the low
  *            nibble holds the even k.
  *   steps    [N][K/32] output bf16 step per group: the smallest step whose
- *            grid reproduces all 32 stored values.
+ *            grid reproduces all 32 stored values; when no bf16 step does (a
+ *            trained step that is not a bf16 value), the candidate step whose
+ *            nearest codes (clamped to [-8, 7]) reproduce the most values,
+ *            the smaller on ties. Candidates: |w_i| / p, p in {1, 2, 4, 8},
+ *            and the 17 bf16 values nearest absmax/a, a in {3, 5, 6, 7}.
  *   d_n_ambiguous  device int64 output: number of groups not recovered
- *            unambiguously (all-zero group, several steps fit, or no power-
- *            of-two code so the step came from a neighbour search, or no 4-bit
- *            grid fits and codes are nearest on step bf16(absmax/7)). May be
- *            NULL.
+ *            unambiguously (all-zero group, several steps fit, no power-of-two
+ *            code so the step came from the neighbour search, or no 4-bit
+ *            grid fits). May be NULL.
  * Requires K % 32 == 0. */
 int qlin_repack_q4_0(const qlin_bf16* w, int64_t N, int64_t K, uint8_t* codes, qlin_bf16* steps,
                      int64_t* d_n_ambiguous, qlin_stream_t stream);

@@ -22,6 +22,9 @@ namespace qlin {
 // A value whose code is +-1, +-2, +-4 or -8 is step * 2^p exactly, so the
 // trained step is among |w_i| * 2^-p (p = 0..3). The smallest step whose grid
 // (codes rint(w/step) in [-8, 7]) reproduces all 32 stored bf16 values wins.
+// When no bf16 step reproduces the whole group (a trained step that is not a
+// bf16 value), the candidate step whose nearest codes reproduce the most
+// stored values is kept, the smaller on ties.
 // ----------------------------------------------------------------------------
 __device__ bool grid_fits(const uint32_t (&w)[32], float step) {
   if (!(step > 0.0f)) return false;
@@ -32,6 +35,19 @@ __device__ bool grid_fits(const uint32_t (&w)[32], float step) {
     if (f32_bf16_rne(q * step) != w[j]) return false;
   }
   return true;
+}
+
+// Stored values reproduced by the nearest codes on `step`, clamped to
+// [-8, 7] (0 for a step that is not finite and positive).
+__device__ int grid_count(const uint32_t (&w)[32], float step) {
+  if (!(step > 0.0f) || !(step < __builtin_inff())) return 0;
+  int n = 0;
+#pragma unroll 4
+  for (int j = 0; j < 32; ++j) {
+    const float q = fminf(fmaxf(__builtin_rintf(bf16_f32(w[j]) / step), -8.0f), 7.0f);
+    n += f32_bf16_rne(q * step) == w[j];
+  }
+  return n;
 }
 
 __global__ __launch_bounds__(256) void zero_i64_kernel(int64_t* p) { *p = 0; }
@@ -89,8 +105,28 @@ __global__ __launch_bounds__(256) void repack_q4_0_kernel(const uint16_t* __rest
     }
     bool fallback = false;
     if (amax > 0.0f && !(best < __builtin_inff())) {
-      best = bf16_f32(f32_bf16_rne(amax / 7.0f));  // no 4-bit grid fits
+      // no 4-bit grid fits: the candidate that reproduces the most values
       fallback = true;
+      int most = -1;
+      for (int i = 0; i < 32; ++i) {
+        const float a = fabsf(bf16_f32(v[i]));
+        if (a == 0.0f) continue;
+        float s = a;
+        for (int p = 0; p < 4; ++p, s *= 0.5f) {
+          const int n = grid_count(v, s);
+          if (n > most || (n == most && s < best)) { most = n; best = s; }
+        }
+      }
+      const float div[4] = {3.0f, 5.0f, 6.0f, 7.0f};
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t c0 = f32_bf16_rne(amax / div[a]);
+        for (int d = -8; d <= 8; ++d) {
+          const float s = bf16_f32((c0 + (uint32_t)d) & 0xFFFFu);
+          if (!(s > 0.0f) || !(s < __builtin_inff())) continue;
+          const int n = grid_count(v, s);
+          if (n > most || (n == most && s < best)) { most = n; best = s; }
+        }
+      }
     }
     // codes on the chosen step
     uint32_t packed[4] = {0, 0, 0, 0};
