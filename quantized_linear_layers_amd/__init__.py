@@ -119,33 +119,49 @@ _FMT = {"e4m3": E4M3, "e4m3fnuz": E4M3FNUZ, "int8": INT8, E4M3: E4M3, E4M3FNUZ: 
         INT8: INT8}
 
 # ---------------------------------------------------------------- workspace
-_ws_cache: dict[int, torch.Tensor] = {}
+# Buffers are cached per (device, stream): calls on one stream are ordered,
+# so they may share a buffer, while calls on two streams may overlap and
+# must not share split-K counters, partial sums or MoE stage data. A buffer
+# that a call outgrows is replaced by one at least twice its size, and the
+# old one is kept alive until the process ends: a HIP graph captured
+# earlier, or a kernel still queued on the stream, may hold its address.
+# (The retired buffers add up to less than the live one.)
+_ws_cache: dict[tuple[int, int], torch.Tensor] = {}
+_scratch_cache: dict[tuple[int, int], torch.Tensor] = {}
+_retired: list[torch.Tensor] = []
+
+
+def _cache_key(device: torch.device) -> tuple[int, int]:
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return idx, torch.cuda.current_stream(idx).cuda_stream
+
+
+def _cached(cache, nbytes: int, device: torch.device, zero: bool) -> torch.Tensor:
+    key = _cache_key(device)
+    ws = cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        size = max(nbytes, 1 << 20, 0 if ws is None else 2 * ws.numel())
+        new = (torch.zeros if zero else torch.empty)(size, dtype=torch.uint8,
+                                                     device=torch.device("cuda", key[0]))
+        if ws is not None:
+            _retired.append(ws)
+        cache[key] = ws = new
+    return ws
 
 
 def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
-    """Zero-initialised per-device workspace of at least nbytes (kept for
-    reuse; the library leaves its counter area zero after every call)."""
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _ws_cache.get(idx)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _ws_cache[idx] = ws
-    return ws
-
-
-_scratch_cache: dict[int, torch.Tensor] = {}
+    """Zero-initialised workspace of at least nbytes for the current stream
+    of `device` (kept for reuse; the library leaves its counter area zero
+    after every call)."""
+    return _cached(_ws_cache, nbytes, device, True)
 
 
 def scratch(nbytes: int, device: torch.device) -> torch.Tensor:
-    """Per-device scratch of at least nbytes for calls that overwrite their
-    whole workspace (the MoE blocks). Kept apart from `workspace`, whose
-    counter area the split-K GEMMs need to find zero."""
-    idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _scratch_cache.get(idx)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _scratch_cache[idx] = ws
-    return ws
+    """Scratch of at least nbytes for the current stream of `device`, for
+    calls that overwrite their whole workspace (the MoE blocks). Kept apart
+    from `workspace`, whose counter area the split-K GEMMs need to find
+    zero."""
+    return _cached(_scratch_cache, nbytes, device, False)
 
 
 def workspace_bytes(op: int, M: int, N: int, K: int) -> int:
