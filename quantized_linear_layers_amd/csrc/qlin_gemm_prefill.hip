@@ -1173,9 +1173,11 @@ int launch_prefill(int kind, const void* a, int64_t lda, const float* sa, const 
     if (big) launch_prefill_big<kGemmI8>(g, st);
     else launch_prefill_t<kGemmI8, 128, 128, 2, 2>(g, st);
   } else {
+    // the persistent kernel loads the group steps as dwords straight into
+    // LDS: it needs 4-byte aligned steps (the ABI accepts 2-byte alignment)
     const int tm = (int)((M + 255) / 256), tn = (int)((N + 255) / 256);
     if (tm * tn >= device_cus() / 2 && K % 64 == 0 && K >= 128 && (uint64_t)M * (uint64_t)lda * 2 < (1ull << 31) &&
-        (uint64_t)N * (uint64_t)K / 2 < (1ull << 31))
+        (uint64_t)N * (uint64_t)K / 2 < (1ull << 31) && ((uintptr_t)wsc & 3) == 0)
       prefill_w4_kernel<<<dim3((unsigned)std::min(tm * tn, device_cus())), 256, 0, st>>>(g, tm, tn);
     else
       launch_prefill_t<kGemmW4, 128, 128, 2, 2>(g, st);
