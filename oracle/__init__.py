@@ -69,6 +69,7 @@ def _load():
         "qo_moe_w4a16": (None, [P, I64, I64, I64, I64, C.c_int, P, P, P, P, P, P, P, P, P, P]),
         "qo_embed_q4": (None, [P, I64, P, P, I64, I64, P]),
         "qo_max_threads": (C.c_int, []),
+        "qo_set_threads": (None, [C.c_int]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -391,3 +392,8 @@ def embed_q4(ids, packed, steps):
 
 def max_threads() -> int:
     return _load().qo_max_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (timing only)."""
+    _load().qo_set_threads(int(n))

@@ -836,3 +836,13 @@ int qo_max_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads of the following parallel loops (timing of the benchmark's CPU
+ * baseline on a given core count; no effect on any result). */
+void qo_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
