@@ -272,6 +272,25 @@ int qlin_moe_fp8(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E,
                  const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y, void* ws,
                  size_t ws_bytes, qlin_stream_t stream);
 
+/* Allocation-free variant of qlin_moe_fp8, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same block, kernels and results,
+ * with the stage buffers in a static device array that the library holds on
+ * each GPU it runs on, QLIN_MOE_NOALLOC_MAX_BYTES bytes, until the process
+ * ends. The caller passes inputs and outputs only. A call whose
+ * qlin_moe_workspace_bytes(T, H, I, E, topk) exceeds the array returns
+ * QLIN_ERR_WORKSPACE (E=128, H=2048, I=768, top-8 needs about 50 MiB at
+ * T = 512). Every call on one GPU uses that GPU's array, which keeps what
+ * the last call wrote: calls that overlap in time on one GPU (two streams,
+ * two host threads) race, and the caller must order them. The array's
+ * device address is looked up on the first call on each device; no call
+ * allocates or frees memory. Other errors as for qlin_moe_fp8. */
+#define QLIN_MOE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int qlin_moe_fp8_noalloc(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                         const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                         const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y,
+                         qlin_stream_t stream);
+
 /* The same block with the SwiGLU-OAI activation in place of SiLU(g) * u
  * ([PR]: the fp8 MoE config carries gemm1_alpha / gemm1_beta, 1.702 / 1.0
  * for MiniMax-M3, and a clamp limit):

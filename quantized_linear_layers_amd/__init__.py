@@ -59,6 +59,8 @@ _SIGS = {
     "qlin_moe_workspace_layout": (_INT, [_I64, _I64, _I64, _I64, _INT, C.POINTER(_SZ)]),
     "qlin_moe_fp8": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P, _P,
                             _SZ, _P]),
+    "qlin_moe_fp8_noalloc": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P, _P,
+                                    _P]),
     "qlin_moe_fp8_swiglu_oai": (_INT, [_P, _I64, _I64, _I64, _I64, _INT, _P, _P, _P, _P, _P, _P,
                                        C.c_float, C.c_float, C.c_float, _P, _P, _SZ, _P]),
     "qlin_moe_w4a16_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64, _INT]),
@@ -432,6 +434,38 @@ def moe_fp8(x, topk_ids, topk_w, w13, s13, w2, s2, return_stages=False, swiglu_o
                   aq=view(o[3], R * I, torch.uint8).view(R, I), sa=view(o[4], R, torch.float32),
                   d=view(o[5], R * H, torch.float32).view(R, H))
     return y, stages
+
+
+MOE_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def moe_fp8_noalloc(x, topk_ids, topk_w, w13, s13, w2, s2, out=None):
+    """The FP8 MoE block through the allocation-free entry point: stage
+    buffers in the library's static per-GPU array (calls that overlap on one
+    GPU race). `out` may pass a preallocated y [T,H] bf16."""
+    _check(x, "x", torch.bfloat16, 2)
+    _check(topk_ids, "topk_ids", torch.int32, 2)
+    _check(topk_w, "topk_w", torch.float32, 2)
+    _check(w13, "w13", torch.uint8, 3)
+    _check(s13, "s13", torch.float32, 2)
+    _check(w2, "w2", torch.uint8, 3)
+    _check(s2, "s2", torch.float32, 2)
+    T, H = x.shape
+    E, I2, H2 = w13.shape
+    I = I2 // 2
+    topk = topk_ids.shape[1]
+    if H2 != H or w2.shape != (E, H, I) or s13.shape != (E, I2) or s2.shape != (E, H) or \
+            topk_w.shape != topk_ids.shape or topk_ids.shape[0] != T:
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check(out, "out", torch.bfloat16, 2)
+        if out.shape != (T, H):
+            raise ValueError("out shape mismatch")
+    _call("qlin_moe_fp8_noalloc", _ptr(x), T, H, I, E, topk, _ptr(topk_ids), _ptr(topk_w), _ptr(w13),
+          _ptr(s13), _ptr(w2), _ptr(s2), _ptr(out), _stream(x.device))
+    return out
 
 
 def moe_w4a16(x, topk_ids, topk_w, codes13, steps13, codes2, steps2, return_stages=False):

@@ -304,22 +304,32 @@ int qlin_moe_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t E, int to
   return QLIN_OK;
 }
 
-static int moe_fp8_call(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+// Arguments of the FP8 MoE calls other than the workspace; 1 = nothing to
+// do (T == 0), else a status.
+static int moe_fp8_args(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
                         const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
-                        const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y,
-                        void* ws, size_t ws_bytes, qlin_stream_t stream, const MoeAct& act) {
+                        const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y) {
   QLIN_CHECK(T >= 0 && H > 0 && I > 0 && E > 0 && topk > 0 && H % 32 == 0 && I % 32 == 0 &&
                  E <= 4096 && T * topk <= 0x7FFFFFFF && topk <= E,
              QLIN_ERR_SHAPE);
-  if (T == 0) return QLIN_OK;
+  if (T == 0) return 1;
   QLIN_CHECK(x && topk_ids && topk_w && w13 && s13 && w2 && s2 && y, QLIN_ERR_ARG);
   QLIN_CHECK(a16(x) && a16(w13) && a16(w2) && a16(y) && ((uintptr_t)topk_ids & 3) == 0 &&
                  ((uintptr_t)topk_w & 3) == 0 && ((uintptr_t)s13 & 3) == 0 &&
                  ((uintptr_t)s2 & 3) == 0,
              QLIN_ERR_ALIGN);
+  return QLIN_OK;
+}
+
+static int moe_fp8_call(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                        const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                        const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y,
+                        void* ws, size_t ws_bytes, qlin_stream_t stream, const MoeAct& act) {
+  int rc = moe_fp8_args(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y);
+  if (rc) return rc == 1 ? QLIN_OK : rc;
   QLIN_CHECK(ws && ws_bytes >= qlin_moe_workspace_bytes(T, H, I, E, topk), QLIN_ERR_WORKSPACE);
   QLIN_CHECK(((uintptr_t)ws & 255) == 0, QLIN_ERR_ALIGN);
-  int rc = device_ok();
+  rc = device_ok();
   if (rc) return rc;
   return launch_moe_fp8(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y, ws,
                         as_stream(stream), act);
@@ -331,6 +341,22 @@ int qlin_moe_fp8(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E,
                  size_t ws_bytes, qlin_stream_t stream) {
   return moe_fp8_call(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y, ws, ws_bytes,
                       stream, MoeAct{});
+}
+
+int qlin_moe_fp8_noalloc(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,
+                         const int32_t* topk_ids, const float* topk_w, const uint8_t* w13,
+                         const float* s13, const uint8_t* w2, const float* s2, qlin_bf16* y,
+                         qlin_stream_t stream) {
+  int rc = moe_fp8_args(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y);
+  if (rc) return rc == 1 ? QLIN_OK : rc;
+  QLIN_CHECK(qlin_moe_workspace_bytes(T, H, I, E, topk) <= kMoeScratchBytes, QLIN_ERR_WORKSPACE);
+  rc = device_ok();
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = moe_scratch_ptr(&ws);
+  if (rc) return rc;
+  return launch_moe_fp8(x, T, H, I, E, topk, topk_ids, topk_w, w13, s13, w2, s2, y, ws,
+                        as_stream(stream), MoeAct{});
 }
 
 int qlin_moe_fp8_swiglu_oai(const qlin_bf16* x, int64_t T, int64_t H, int64_t I, int64_t E, int topk,

@@ -73,6 +73,12 @@ int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E
                    const int32_t* ids, const float* wts, const uint8_t* w13, const float* s13,
                    const uint8_t* w2, const float* s2, uint16_t* y, void* ws, hipStream_t st,
                    const MoeAct& act = MoeAct{});
+// Allocation-free FP8 MoE (qlin_moe_fp8_noalloc): the stage buffers live in
+// a static device array of this many bytes on each GPU (qlin_moe.hip).
+constexpr size_t kMoeScratchBytes = QLIN_MOE_NOALLOC_MAX_BYTES;
+// Device address of the current GPU's scratch array, resolved once per
+// device (a host-side reference to the array itself is not an address).
+int moe_scratch_ptr(void** ptr);
 struct MoeW4Layout {
   size_t act, d, off, rows, total;
 };

@@ -20,11 +20,37 @@
 // Stay Slow") runs the same grouped GEMMs on bf16 activations and int4
 // expert banks unpacked in the kernel: no quantisation stages, and
 // act = bf16(SiLU(g) * u) is written by the gate_up epilogue.
+#include <mutex>
+
 #include "qlin_device.h"
 #include "qlin_internal.h"
 #include "qlin_skinny.h"
 
 namespace qlin {
+
+// Stage buffers of the allocation-free FP8 MoE entry point: one array per
+// GPU, alive until the process ends. Every call on a GPU reuses it (calls
+// that overlap on one GPU race) and overwrites what the previous call left;
+// no part of it has to start at zero.
+static __device__ __align__(256) uint8_t scratch[kMoeScratchBytes];
+
+int moe_scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return QLIN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return QLIN_OK;
+}
 
 MoeLayout moe_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk) {
   const int64_t R = T * topk;
