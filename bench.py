@@ -888,8 +888,10 @@ def summarize_pmc(dirs, out_md, cmds):
                 return round(c[a] / c[b], 3) if a in c and b in c and c[b] else None
 
             mfma_busy = None
-            if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c and c["GRBM_GUI_ACTIVE"]:
-                mfma_busy = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * c["GRBM_GUI_ACTIVE"]), 3)
+            if c.get("SQ_VALU_MFMA_BUSY_CYCLES") and c.get("SQ_WAVE_CYCLES") and c.get("SQ_WAVES"):
+                # SQ_WAVE_CYCLES counts quad-cycles: one wave's lifetime in cycles
+                life = 4.0 * c["SQ_WAVE_CYCLES"] / c["SQ_WAVES"]
+                mfma_busy = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * life), 3)
             l2 = None
             if "TCC_HIT_sum" in c and "TCC_MISS_sum" in c and (c["TCC_HIT_sum"] + c["TCC_MISS_sum"]):
                 l2 = round(c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"]), 3)
@@ -903,7 +905,11 @@ def summarize_pmc(dirs, out_md, cmds):
             trow["kernels"].append(k)
 
             def f(v):
-                return "-" if v is None else (f"{v:.1f}" if isinstance(v, float) else str(v))
+                if v is None:
+                    return "-"
+                if isinstance(v, float):
+                    return f"{v:.3f}" if abs(v) < 10 else f"{v:.1f}"
+                return str(v)
 
             lines.append("| " + " | ".join([
                 name, k["kernel"], str(k["grid"]), str(k["vgpr"]), f(k["us"]), f(k["fetch_kib"]),
@@ -933,7 +939,10 @@ def summarize_pmc(dirs, out_md, cmds):
             "write_factor (KiB x 1024), the factors being what the counters read for a 256 MiB device copy "
             "(known bytes). Shares are of SQ_WAVE_CYCLES: VALU / LDS = cycles with such an instruction "
             "active, wait = cycles waiting on an instruction's operands; MFMA busy = "
-            "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE); VALU / MFMA counts instructions; "
+            "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x one wave's lifetime, 4 x SQ_WAVE_CYCLES / SQ_WAVES, "
+            "SQ_WAVE_CYCLES counting quad-cycles): the busy share of the MFMA pipes for the persistent "
+            "kernels with one wave per SIMD (prefill_*, hipBLASLt), a lower bound elsewhere; VALU / MFMA "
+            "counts instructions; "
             "L2 hit = TCC hits / (hits + misses). `-`: the counter was not in the passes given.\n\n")
         fh.write("\n".join(lines) + "\n\n")
         fh.write("Machine-readable table (bench.py reads `hbm_bytes` per row; `sources_sha256` hashes the "
