@@ -352,6 +352,7 @@ static auto with_decode_inst(int kind, int MB, int NB, bool wk, bool sb, F&& f) 
 constexpr size_t kCounterBytes = kGemmCounterBytes;
 
 size_t decode_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K) {
+  if (kind == kGemmW4 && w4_few_applies(M, N, K)) return 0;
   const DecodeCfg c = decode_cfg(kind, M, N, K);
   if (c.S <= 1) return 0;
   return kCounterBytes + round_up((size_t)c.S * M * N * 4, 256);
@@ -371,6 +372,8 @@ struct LaunchFn {
 int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const void* w,
                   const void* wsc, int64_t M, int64_t N, int64_t K, void* y, int out_f32,
                   void* ws, size_t ws_bytes, hipStream_t st) {
+  if (kind == kGemmW4 && w4_few_applies(M, N, K))
+    return launch_w4_few(a, lda, w, wsc, M, N, K, y, out_f32, st);
   const DecodeCfg c = decode_cfg(kind, M, N, K);
   GemmArgs g{};
   g.A = reinterpret_cast<const uint8_t*>(a);

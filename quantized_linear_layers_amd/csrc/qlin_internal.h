@@ -51,6 +51,11 @@ size_t gemm_workspace_bytes(int kind, int64_t M, int64_t N, int64_t K);
 // Split-K arrival counters occupy the first kGemmCounterBytes of every GEMM
 // workspace (zero between calls); partial sums follow them.
 constexpr size_t kGemmCounterBytes = 65536;
+// W4A16 at M <= 64, K % 256 == 0, on layers too small for one wave per 16
+// columns to fill the device (qlin_gemm_w4_decode.hip): no workspace.
+bool w4_few_applies(int64_t M, int64_t N, int64_t K);
+int launch_w4_few(const void* a, int64_t lda, const void* codes, const void* steps, int64_t M,
+                  int64_t N, int64_t K, void* y, int out_f32, hipStream_t st);
 int launch_gemm(int kind, const void* a, int64_t lda, const float* sa, const void* w,
                 const void* wsc, int64_t M, int64_t N, int64_t K, void* y, int out_f32, void* ws,
                 size_t ws_bytes, hipStream_t st);

@@ -101,18 +101,24 @@ def run_decode(q, oracle, N, K, Ms, misalign=False, extra_m1=()):
 
 
 # ------------------------------------------------------------------ decode paths
-# The launch rules at 256 CUs: one 16-row block (M <= 16) on a layer of at
-# most 12224 columns splits K over the 4 waves of a workgroup (WK); wider
-# layers give each wave its own columns; M = 33..64 on a layer of at least
-# 24449 columns runs two column blocks per wave in 8-wave workgroups. K % 256
-# == 0 with 16-byte aligned step rows loads the steps in bulk, otherwise per
-# unit.
+# The launch rules at 256 CUs: with K % 256 == 0, M <= 16 on a layer of
+# fewer than 16384 columns, and M = 17..64 on one of 6145..8192 columns, run
+# the small-layer kernel (waves splitting K in 1, 2 or 4 parts; 1, 4, 8, 16,
+# 32 or 64 staged rows). Otherwise the streaming core: one
+# 16-row block (M <= 16) on a layer of at most 12224 columns splits K over
+# the 4 waves of a workgroup (WK); wider layers give each wave its own
+# columns; M = 33..64 on a layer of at least 24449 columns runs two column
+# blocks per wave in 8-wave workgroups. K % 256 == 0 with 16-byte aligned
+# step rows loads the steps in bulk, otherwise per unit.
 DECODE_CASES = [
     # id, N, K, Ms, misalign, M=1 rows
-    ("wk_bulk", 7808, 256, (16,), False, (0, 1, 131, 255)),
+    ("small_layer_one_unit", 7808, 256, (16,), False, (0, 1, 131, 255)),
+    ("small_layer_k_parts", 1952, 1024, (1, 4, 8, 16), False, ()),
+    ("small_layer_unaligned_steps", 7808, 256, (16,), True, (3,)),
+    ("small_layer_32_64_rows", 8192, 512, (32, 48, 64), False, ()),
+    ("small_layer_64_rows_one_part", 8160, 256, (17, 64), False, ()),
     ("wk_per_unit_k288", 6944, 288, (16,), False, (0, 287)),
-    ("wk_per_unit_unaligned", 7808, 256, (16,), True, (3,)),
-    ("wide_mb1_bulk", 12288, 256, (16,), False, (0, 200)),
+    ("wide_mb1_bulk", 16384, 256, (16,), False, (0, 200)),
     ("wide_mb1_per_unit", 12288, 288, (16,), False, ()),
     ("mb2_mb3_mb4_bulk", 4096, 512, (32, 48, 64), False, ()),
     ("mb2_mb4_per_unit", 4096, 288, (32, 64), False, ()),
