@@ -53,7 +53,7 @@ def test_fp8_encoder_dense_sweep(q, oracle, fmt):
 # ------------------------------------------------------------------ quantisers
 @pytest.mark.parametrize("fmt", ["e4m3", "int8", "e4m3fnuz"])
 @pytest.mark.parametrize("case", ["c1", "c2", "c3", "ragged", "zero_rows", "long", "tall_k80", "tall_k768",
-                                  "tall_k2048"])
+                                  "tall_k2048", "tall_k4096", "tall_k4112"])
 def test_quant_act_bit_exact(q, oracle, fmt, case):
     if case == "c1":
         a = gen.linear_config(1)["a"]
@@ -71,8 +71,9 @@ def test_quant_act_bit_exact(q, oracle, fmt, case):
     elif case == "long":
         a = gen.linear_config(1, n=16, k=20480, m=3)["a"]  # rows beyond 16384: two-pass path
     else:
-        # >= 1024 rows of <= 2048 elements: one wave per row (ragged row count
-        # against the four rows of a workgroup, zero rows included)
+        # >= 1024 rows of <= 4096 elements: one wave per row (ragged row count
+        # against the four rows of a workgroup, zero rows included); 4112 is
+        # one chunk past it (a workgroup per row)
         K = int(case[6:])
         a = gen.activations(np.random.default_rng(K), 1027 if K != 2048 else 1024, K).copy()
         a[5] = 0
@@ -798,8 +799,9 @@ def test_gemm_longest_k(q, oracle, fmt):
 
 
 def test_graph_replay_matches_eager(q, oracle):
-    """A captured HIP graph of a split-K W4A16 GEMM (M = 64, 16 column
-    tiles, 4 K splits), an FP8 linear (M = 8) and a W4A16 MoE block, replayed
+    """A captured HIP graph of a W4A16 GEMM (M = 64), a split-K FP8 GEMM
+    (1024 columns: 32 column tiles, 4 K splits), an FP8 linear (M = 8) and a
+    W4A16 MoE block, replayed
     three times with eager calls of other shapes in between: every replay
     equals the eager result bit for bit (the split-K counters are back at
     zero after each call; nothing in the library records a memset)."""
@@ -815,15 +817,19 @@ def test_graph_replay_matches_eager(q, oracle):
     y4 = torch.empty(64, 1024, dtype=torch.bfloat16, device="cuda")
     y8 = torch.empty(8, 1024, dtype=torch.bfloat16, device="cuda")
     ym = torch.empty(24, 256, dtype=torch.bfloat16, device="cuda")
+    ys = torch.empty(2, 1024, dtype=torch.bfloat16, device="cuda")
+    aq, sa = dev(ops8["aq"][:2]), dev(ops8["sa"][:2])
+    assert q.workspace_bytes(q.OP_GEMM_FP8, 2, 1024, 2048) > 0  # split over K
 
     def calls():
         q.gemm_w4a16(a, pk, st, out=y4)
         q.linear_fp8(a[:8], wq, ws, out=y8)
+        q.gemm_fp8(aq, sa, wq, ws, out=ys)
         ym.copy_(q.moe_w4a16(xm, ids, pr, *wm))
 
     calls()
     torch.cuda.synchronize()
-    ref = [host(y4), host(y8), host(ym)]
+    ref = [host(y4), host(y8), host(ym), host(ys)]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -834,12 +840,12 @@ def test_graph_replay_matches_eager(q, oracle):
     with torch.cuda.graph(g):
         calls()
     for rep in range(3):
-        for y in (y4, y8, ym):
+        for y in (y4, y8, ym, ys):
             y.zero_()
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(y4), ref[0]) and np.array_equal(host(y8), ref[1]) and \
-            np.array_equal(host(ym), ref[2]), f"replay {rep}"
+            np.array_equal(host(ym), ref[2]) and np.array_equal(host(ys), ref[3]), f"replay {rep}"
         # eager work of other shapes between replays (another split-K grid)
         q.gemm_w4a16(a[:40], pk, st)
         q.linear_fp8(a[:3], wq, ws)
