@@ -624,8 +624,8 @@ def vocab_rows(q, torch, gen, iters):
 # hardware-counter workloads (run under rocprofv3 --pmc) and their summary
 # ----------------------------------------------------------------------------
 CSRC = os.path.join(ROOT, "quantized_linear_layers_amd", "csrc")
-DECODE_SOURCES = ("qlin_gemm_decode.hip", "qlin_skinny.h", "qlin_device.h", "qlin_quant.hip",
-                  "qlin_abi.hip")
+DECODE_SOURCES = ("qlin_gemm_decode.hip", "qlin_gemm_w4_decode.hip", "qlin_skinny.h", "qlin_device.h",
+                  "qlin_quant.hip", "qlin_abi.hip")
 PREFILL_SOURCES = ("qlin_gemm_prefill.hip", "qlin_device.h", "qlin_quant.hip", "qlin_abi.hip")
 MOE_SOURCES = ("qlin_moe.hip", "qlin_skinny.h", "qlin_device.h", "qlin_quant.hip")
 PMC_SOURCES = {"decode": DECODE_SOURCES, "prefill": PREFILL_SOURCES, "moe": MOE_SOURCES}

@@ -3,7 +3,7 @@
 // From E2B to 31B" article, format table: int8 activations per token).
 //   s = max_k |a| / FMAX   (FMAX 448 for OCP E4M3, 127 for int8)
 //   q = nearest-even E4M3 code of a / s (saturating)  or  clamp(rint(a/s)).
-// Many rows of up to 4096 elements: one wave per row; otherwise one
+// Many rows of up to 2048 elements: one wave per row; otherwise one
 // workgroup per row. The row is read once into registers (up to 16384
 // elements), reduced to its absmax, then encoded and written.
 #include "qlin_device.h"
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const uint16_t* __
   }
 }
 
-// Rows of at most 4096 elements: one wave per row (four rows per
+// Rows of at most 2048 elements: one wave per row (four rows per
 // workgroup), CPL 16-byte chunks per lane held in registers, the absmax
 // reduced within the wave (no LDS, no barrier). The same absmax, scale and
 // encoder as above, so the same codes.
@@ -180,8 +180,6 @@ static void launch_quant_fmt(const uint16_t* a, int64_t M, int64_t K, int64_t ld
     quant_rows_wave_kernel<FMT, 2><<<wgrid, kQThreads, 0, st>>>(a, M, K, lda, q, s);
   else if (tall && chunks <= 256)
     quant_rows_wave_kernel<FMT, 4><<<wgrid, kQThreads, 0, st>>>(a, M, K, lda, q, s);
-  else if (tall && chunks <= 512)  // K=4096 prefill rows: 8 KB per wave in registers
-    quant_rows_wave_kernel<FMT, 8><<<wgrid, kQThreads, 0, st>>>(a, M, K, lda, q, s);
   else if (chunks <= 1 * kQThreads)
     quant_act_kernel<FMT, 1><<<grid, kQThreads, 0, st>>>(a, K, lda, q, s);
   else if (chunks <= 2 * kQThreads)

@@ -71,9 +71,9 @@ def test_quant_act_bit_exact(q, oracle, fmt, case):
     elif case == "long":
         a = gen.linear_config(1, n=16, k=20480, m=3)["a"]  # rows beyond 16384: two-pass path
     else:
-        # >= 1024 rows of <= 4096 elements: one wave per row (ragged row count
-        # against the four rows of a workgroup, zero rows included); 4112 is
-        # one chunk past it (a workgroup per row)
+        # >= 1024 rows of <= 2048 elements: one wave per row (ragged row count
+        # against the four rows of a workgroup, zero rows included); 4096 and
+        # 4112 run a workgroup per row, two chunks per thread and a ragged one
         K = int(case[6:])
         a = gen.activations(np.random.default_rng(K), 1027 if K != 2048 else 1024, K).copy()
         a[5] = 0
