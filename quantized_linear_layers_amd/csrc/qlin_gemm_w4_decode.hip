@@ -312,13 +312,19 @@ static void w4few_launch(const W4FewArgs& a, hipStream_t st) {
   decode_w4_few_kernel<NB, MB, DEPTH, NC, NQ, NR, MR, CK><<<dim3((unsigned)grid), 256, 0, st>>>(a);
 }
 
-// Launch rule, as measured at K=2048, N=8192 (one 16-column block per
-// wave): the waves split K in 2 parts at M = 1 and in 4 above (M = 1: 5.2 us
-// against 5.6 in 4 parts; M = 8: 6.2 us against 7.1 in 2 parts).
+// Launch rule, as measured (one 16-column block per wave): at M = 1 the
+// fewest K parts that give every SIMD a wave (K=2048, N=8192: 2 parts, 5.2
+// us against 5.6 in 4; K=4096, N=14336: 2 parts, 11.4 us against 14.7 in 1
+// and 13.9 in 4; K=14336, N=4096: 4 parts, 14.8 us against 23.4 in 2);
+// above, 4 parts (K=2048, N=8192, M = 8: 6.2 us against 7.1 in 2), and 2
+// at 16 rows.
 template <int MR, int CK>
 static void w4few_rows(W4FewArgs& a, hipStream_t st) {
   const int units = a.K / 256;
-  int nq = MR <= 1 ? 2 : 4;
+  const int64_t blocks = (a.N + 15) / 16, simds = 4 * (int64_t)w4few_cus();
+  int nq = 4;
+  if (MR <= 1)
+    for (nq = 1; nq < 4 && blocks * nq < simds;) nq *= 2;
   if (MR == 16) nq = 2;  // 16 rows x 4 parts would not fit LDS twice
   nq = std::max(1, std::min(nq, units));
   if (nq == 3) nq = 2;

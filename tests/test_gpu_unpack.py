@@ -115,7 +115,7 @@ DECODE_CASES = [
     ("small_layer_one_unit", 7808, 256, (16,), False, (0, 1, 131, 255)),
     ("small_layer_k_parts", 1952, 1024, (1, 4, 8, 16), False, ()),
     ("small_layer_unaligned_steps", 7808, 256, (16,), True, (3,)),
-    ("small_layer_32_64_rows", 8192, 512, (32, 48, 64), False, ()),
+    ("small_layer_32_64_rows", 8192, 512, (32, 48, 64), False, (0, 300)),
     ("small_layer_64_rows_one_part", 8160, 256, (17, 64), False, ()),
     ("wk_per_unit_k288", 6944, 288, (16,), False, (0, 287)),
     ("wide_mb1_bulk", 16384, 256, (16,), False, (0, 200)),
