@@ -33,6 +33,8 @@ Counter tools (rocprofv3 runs of committed code):
   --pmc-workload prefill|moe   the M=8192 GEMMs or the MoE blocks
   --summarize-pmc DIR ...  turn the counter CSVs of those runs into the
                            markdown summaries kept under profiles/
+  --summarize-trace CSV    group a rocprofv3 --kernel-trace CSV by kernel
+                           and grid
 """
 
 from __future__ import annotations
@@ -83,6 +85,10 @@ def parse():
     ap.add_argument("--pmc-out", default=None, help="markdown file written by --summarize-pmc")
     ap.add_argument("--pmc-cmd", action="append", default=[],
                     help="the rocprofv3 command of each pass, quoted in the summary")
+    ap.add_argument("--summarize-trace", metavar="CSV", default=None,
+                    help="print the dispatches of a rocprofv3 --kernel-trace CSV grouped by kernel "
+                         "and grid (count, average and minimum duration), largest total first")
+    ap.add_argument("--trace-top", type=int, default=70, help="groups printed by --summarize-trace")
     return ap.parse_args()
 
 
@@ -807,6 +813,37 @@ def _short(kernel):
     return k.replace("qlin::", "")
 
 
+def summarize_trace(csv_path, top):
+    """Group the dispatches of a kernel-trace CSV by kernel (name without
+    namespace and argument list) and grid in workgroups; one line per group,
+    largest total duration first."""
+    import csv
+    import collections
+
+    def short(name):
+        name = name.replace("qlin::", "")
+        depth = 0
+        for i, ch in enumerate(name):
+            if ch == "<":
+                depth += 1
+            elif ch == ">":
+                depth -= 1
+            elif ch == "(" and depth == 0:
+                return name[:i][:60]
+        return name[:60]
+
+    groups = collections.defaultdict(list)
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            wx = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            wy = int(r["Grid_Size_Y"]) // max(1, int(r["Workgroup_Size_Y"]))
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups[(short(r["Kernel_Name"]), wx, wy)].append(us)
+    items = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
+    for (name, wx, wy), d in items:
+        print(f"{name:60s} grid=({wx},{wy}) n={len(d):5d} avg={sum(d) / len(d):10.2f}us min={min(d):10.2f}us")
+
+
 def summarize_pmc(dirs, out_md, cmds):
     """Counter summary of one workload: dispatches after the marker are
     assigned, in order, to the plan's rows (launches x kernels per call);
@@ -1077,6 +1114,9 @@ def main():
     a = parse()
     if a.summarize_pmc:
         summarize_pmc(a.summarize_pmc, a.pmc_out, a.pmc_cmd)
+        return
+    if a.summarize_trace:
+        summarize_trace(a.summarize_trace, a.trace_top)
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this build measures the "
