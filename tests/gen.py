@@ -89,6 +89,22 @@ def activations(rng: np.random.Generator, m: int, k: int) -> np.ndarray:
     return to_bf16_bits(x)
 
 
+def wide_range_rows(rng: np.random.Generator, m: int, k: int) -> np.ndarray:
+    """bf16 bits [m,k] spread over the whole bf16 range: row i draws a top
+    exponent field e_i in [1, 254] and a width w_i in [0, 40]; each value
+    takes an exponent field uniform in [max(0, e_i - w_i), e_i] (field 0:
+    subnormals), a uniform mantissa and sign; 1 % of values are +0 or -0."""
+    e_hi = rng.integers(1, 255, size=(m, 1))
+    w = rng.integers(0, 41, size=(m, 1))
+    e = np.maximum(e_hi - rng.integers(0, 1 << 30, size=(m, k)) % (w + 1), 0)
+    mant = rng.integers(0, 128, size=(m, k))
+    sign = rng.integers(0, 2, size=(m, k))
+    bits = (sign << 15) | (e << 7) | mant
+    zero = rng.random(size=(m, k)) < 0.01
+    bits[zero] = sign[zero] << 15
+    return bits.astype(np.uint16)
+
+
 def route_topk(logits: np.ndarray, topk: int):
     """Router stand-in: softmax over experts, top-k ids and probabilities.
 

@@ -53,9 +53,17 @@ def test_fp8_encoder_dense_sweep(q, oracle, fmt):
 # ------------------------------------------------------------------ quantisers
 @pytest.mark.parametrize("fmt", ["e4m3", "int8", "e4m3fnuz"])
 @pytest.mark.parametrize("case", ["c1", "c2", "c3", "ragged", "zero_rows", "long", "tall_k80", "tall_k768",
-                                  "tall_k2048", "tall_k4096", "tall_k4112"])
+                                  "tall_k2048", "tall_k4096", "tall_k4112", "wide_wave", "wide_wg",
+                                  "wide_long"])
 def test_quant_act_bit_exact(q, oracle, fmt, case):
-    if case == "c1":
+    """Codes and scales bit for bit. The wide_* rows span the whole bf16
+    range (subnormals, signed zeros, scales below 2^-100 that take the
+    kernels' division fallback) on each kernel: a wave per row (1030 rows of
+    512), a workgroup per row (64 of 4096) and the two-pass rows (20480)."""
+    if case.startswith("wide_"):
+        m, k = {"wide_wave": (1030, 512), "wide_wg": (64, 4096), "wide_long": (6, 20480)}[case]
+        a = gen.wide_range_rows(np.random.default_rng(m + k), m, k)
+    elif case == "c1":
         a = gen.linear_config(1)["a"]
     elif case == "c2":
         a = gen.linear_config(2, n=16)["a"]
