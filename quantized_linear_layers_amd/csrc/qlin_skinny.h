@@ -187,7 +187,11 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   // wave's first row is valid, and valid rows are a prefix). Only the
   // W4A16 path skips the others (4x the activation traffic per weight
   // byte); for fp8/int8 the branches cost more registers than they save.
-  uint4 aset[2][kPer];
+  // register sets of activation chunks in flight: two (chunk ci + 2 loaded
+  // at the start of chunk ci) for fp8/int8, one (chunk ci + 1) for W4A16,
+  // whose bf16 chunks take twice the registers
+  constexpr int kSets = W4 ? 1 : 2;
+  uint4 aset[kSets][kPer];
   bool qv[kPer];
 #pragma unroll
   for (int q = 0; q < kPer; ++q) qv[q] = !W4 || __builtin_amdgcn_readfirstlane(am[q]) != 0u;
@@ -296,7 +300,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   // weight ring filled
   sload(0);
   aload(0, aset[0]);
-  aload(1, aset[1]);
+  if constexpr (kSets == 2) aload(1, aset[1]);
   SkinnySlot<KIND, NB> ring[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) wload(ring[d], d);
@@ -311,9 +315,9 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   block_sync();
 
   // ---- main loop over whole rounds of DEPTH units. Activation chunk ci
-  // uses LDS buffer ci & 1 and register set ci & 1; at its start the set is
-  // refilled with chunk ci + 2, after its last unit chunk ci + 1 goes to the
-  // other buffer. Each unit: its registers go to the wave's slot, the ring
+  // uses LDS buffer ci & 1 and register set ci % kSets; at its start the
+  // set is refilled with chunk ci + kSets, after its last unit chunk ci + 1
+  // goes to the other buffer. Each unit: its registers go to the wave's slot, the ring
   // slot is refilled DEPTH units ahead (past the range: clamped loads of
   // valid memory, never used), then the unit is multiplied. The scheduling
   // barriers keep each refill right after the write that freed its slot.
@@ -324,7 +328,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int u = rd * DEPTH + d;
-      if (d % UPC == 0) aload(u / UPC + 2, aset[(d / UPC) & 1]);
+      if (d % UPC == 0) aload(u / UPC + kSets, aset[(d / UPC) % kSets]);
       if (d == 0) {
         swrite();
         sload(u + DEPTH);
@@ -335,7 +339,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
       __builtin_amdgcn_sched_barrier(0);
       compute(u, d);
       if (d % UPC == UPC - 1) {
-        awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
+        awrite(aset[((d / UPC) + 1) % kSets], u / UPC + 1, (u / UPC + 1) & 1);
         block_sync();
       }
     }
@@ -348,11 +352,11 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
   for (int d = 0; d < DEPTH - 1; ++d) {
     if (d < rem) {
       const int u = full * DEPTH + d;
-      if (d % UPC == 0) aload(u / UPC + 2, aset[(d / UPC) & 1]);
+      if (d % UPC == 0) aload(u / UPC + kSets, aset[(d / UPC) % kSets]);
       wstage(ring[d]);
       compute(u, d);
       if (d % UPC == UPC - 1 && d + 1 < rem) {
-        awrite(aset[((d / UPC) + 1) & 1], u / UPC + 1, (u / UPC + 1) & 1);
+        awrite(aset[((d / UPC) + 1) % kSets], u / UPC + 1, (u / UPC + 1) & 1);
         block_sync();
       }
     }
