@@ -186,19 +186,26 @@ __global__ __launch_bounds__(256) void decode_w4_few_kernel(const W4FewArgs p) {
       for (int j = 0; j < NB; ++j) st[j] = int4_step(bf16_f32(sl.s[j][h]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // the activation fragments are requested before the unpack, which
+        // covers their LDS latency (scheduling barriers keep the order)
         v8bf af[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           af[mb] = *reinterpret_cast<const v8bf*>(lds + arow[mb] + buf * abuf[mb] + cu * 512 + g * 64 +
                                                   h * 256 + i * 16);
+        __builtin_amdgcn_sched_barrier(0);
+        v8bf bf[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const uint4& cw = frag[j][h];
           const uint32_t word = i == 0 ? cw.x : i == 1 ? cw.y : i == 2 ? cw.z : cw.w;
-          const v8bf bf = dequant8_mix(word, st[j]);
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma_bf16(af[mb], bf, acc[mb][j]);
+          bf[j] = dequant8_mix(word, st[j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma_bf16(af[mb], bf[j], acc[mb][j]);
       }
     }
   };
