@@ -102,15 +102,15 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
     am[q] = row < p.M ? 0xFFFFFFFFu : 0u;
   }
 
-  // epilogue scales of this lane's rows / columns, fetched up front
-  float sav[MB][4], swv[NB];
+  // epilogue scales of this lane's row (one per row block) and its 4
+  // columns per column block (the core's output layout), fetched up front
+  float sav[MB], swv[NB][4];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) sav[mb] = W4 ? 1.0f : p.sa[min(mb * 16 + r, p.M - 1)];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sav[mb][i] = W4 ? 1.0f : p.sa[min(mb * 16 + 4 * g + i, p.M - 1)];
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
-  for (int j = 0; j < NB; ++j) swv[j] = W4 ? 1.0f : p.sw[min(n0 + 16 * j + r, p.N - 1)];
+    for (int i = 0; i < 4; ++i) swv[j][i] = W4 ? 1.0f : p.sw[min(n0 + 16 * j + 4 * g + i, p.N - 1)];
 
   Acc acc[MB][NB];
 #pragma unroll
@@ -154,25 +154,41 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
         if constexpr (KIND == kGemmI8) acci[mb][j][i] = acc[mb][j][i];
         else accf[mb][j][i] = acc[mb][j][i];
       }
-  // Partial sums and the counter use device-scope relaxed atomic accesses,
-  // which bypass the per-XCD L2 caches; a store is complete (vmcnt) once it
-  // is visible device-wide, so waiting for the stores before the counter
-  // increment orders them without a cache-wide write-back fence (a fence
-  // here would flush and invalidate the whole L2 of the XCD on every
-  // workgroup).
+  // Partial sums and the counter use device-scope accesses (the partials:
+  // buffer loads and stores with the sc1 cache policy, which bypass the
+  // per-XCD L2 caches as relaxed device-scope atomics do); a store is
+  // complete (vmcnt) once it is visible device-wide, so waiting for the
+  // stores before the counter increment orders them without a cache-wide
+  // write-back fence (a fence here would flush and invalidate the whole L2
+  // of the XCD on every workgroup). Each lane moves its 4 consecutive
+  // columns as one 16-byte access when the rows allow it.
+  constexpr int kSc1 = 16;  // cache policy: sc1
+  const bool pvec = (p.N & 3) == 0;
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      p.part, (short)0, (int)min((size_t)S * p.M * p.N * 4, (size_t)0x7FFFFFFF), 0x00020000);
+  auto part_off = [&](int sp, int m, int n) { return (uint32_t)((((size_t)sp * p.M + m) * p.N + n) * 4); };
   if (S > 1) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = mb * 16 + r;
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NB; ++j) {
+        const int n = n0 + 16 * j + 4 * g;
+        uint32_t w[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = mb * 16 + 4 * g + i, n = n0 + 16 * j + r;
-          if (owner && m < p.M && n < p.N)
-            __hip_atomic_store(&p.part[((size_t)split * p.M + m) * p.N + n],
-                               KIND == kGemmI8 ? (uint32_t)acci[mb][j][i] : __float_as_uint(accf[mb][j][i]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < 4; ++i) w[i] = KIND == kGemmI8 ? (uint32_t)acci[mb][j][i] : __float_as_uint(accf[mb][j][i]);
+        if (owner && m < p.M) {
+          const uint32_t o = part_off(split, m, n);
+          if (pvec && n + 3 < p.N) {
+            __builtin_amdgcn_raw_buffer_store_b128(v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]}, prs, o, 0, kSc1);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (n + i < p.N) __builtin_amdgcn_raw_buffer_store_b32(w[i], prs, o + 4 * i, 0, kSc1);
+          }
         }
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial sums are visible
     __syncthreads();                // ... and those of the other waves
     if (tid == 0)
@@ -183,29 +199,40 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
     // sum the splits in split order; the loads of up to 4 splits are all
     // issued before the first is consumed (each load is a round trip to
     // memory; clamped addresses, no branches before the sums)
-    const size_t stride = (size_t)p.M * p.N;
-    uint32_t off[MB][NB][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          off[mb][j][i] = (uint32_t)((size_t)min(mb * 16 + 4 * g + i, p.M - 1) * p.N +
-                                     min(n0 + 16 * j + r, p.N - 1));
     for (int s0 = 0; s0 < S; s0 += 4) {
       uint32_t u[4][MB][NB][4];
+      // (one branch around all loads: a branch per load would make the
+      // compiler wait for older loads at every block boundary)
+      if (pvec) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t* q = p.part + (size_t)min(s0 + b, S - 1) * stride;
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int j = 0; j < NB; ++j)
+            for (int j = 0; j < NB; ++j) {
+              const int m = min(mb * 16 + r, p.M - 1), n = min(n0 + 16 * j + 4 * g, p.N - 4);
+              const v4i x = __builtin_amdgcn_raw_buffer_load_b128(prs, part_off(min(s0 + b, S - 1), m, n), 0, kSc1);
+              u[b][mb][j][0] = (uint32_t)x.x;
+              u[b][mb][j][1] = (uint32_t)x.y;
+              u[b][mb][j][2] = (uint32_t)x.z;
+              u[b][mb][j][3] = (uint32_t)x.w;
+            }
+      } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              u[b][mb][j][i] = __hip_atomic_load(&q[off[mb][j][i]], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int m = min(mb * 16 + r, p.M - 1), n = min(n0 + 16 * j + 4 * g + i, p.N - 1);
+                u[b][mb][j][i] = __builtin_amdgcn_raw_buffer_load_b32(prs, part_off(min(s0 + b, S - 1), m, n), 0, kSc1);
+              }
       }
+      // every load above is issued before the first sum (the scheduler would
+      // otherwise interleave them and keep only a few in flight)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (s0 + b >= S) break;
@@ -229,23 +256,43 @@ __global__ __launch_bounds__(64 * NW) void decode_gemm_kernel(const GemmArgs p) 
   }
   if (!owner) return;
 
-  // ---- epilogue
+  // ---- epilogue: each lane writes 4 consecutive columns of its row as one
+  // 16-byte (fp32) or 8-byte (bf16) store when the row segment is aligned
+  // and inside the output, element by element otherwise
+  const bool vec = (p.N & 3) == 0 && ((uintptr_t)p.y & (p.out_f32 ? 15u : 7u)) == 0;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = mb * 16 + r;
+    if (m >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + 16 * j + 4 * g;
+      float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int m = mb * 16 + 4 * g + i, n = n0 + 16 * j + r;
-        if (m < p.M && n < p.N) {
-          float v;
-          if constexpr (KIND == kGemmW4) v = accf[mb][j][i];
-          else if constexpr (KIND == kGemmI8) v = ((float)acci[mb][j][i] * sav[mb][i]) * swv[j];
-          else v = (accf[mb][j][i] * sav[mb][i]) * swv[j];
-          if (p.out_f32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = v;
-          else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = (uint16_t)f32_bf16_rne(v);
+        if constexpr (KIND == kGemmW4) v[i] = accf[mb][j][i];
+        else if constexpr (KIND == kGemmI8) v[i] = ((float)acci[mb][j][i] * sav[mb]) * swv[j][i];
+        else v[i] = (accf[mb][j][i] * sav[mb]) * swv[j][i];
+      }
+      const size_t o = (size_t)m * p.N + n;
+      if (vec && n + 3 < p.N) {
+        if (p.out_f32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + o) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) =
+              make_uint2(f32_bf16_rne(v[0]) | (f32_bf16_rne(v[1]) << 16), f32_bf16_rne(v[2]) | (f32_bf16_rne(v[3]) << 16));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (n + i < p.N) {
+            if (p.out_f32) reinterpret_cast<float*>(p.y)[o + i] = v[i];
+            else reinterpret_cast<uint16_t*>(p.y)[o + i] = (uint16_t)f32_bf16_rne(v[i]);
+          }
         }
       }
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------

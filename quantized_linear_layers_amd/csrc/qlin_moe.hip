@@ -242,57 +242,85 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
     for (int j = 0; j < NB; ++j) acc[i][j] = v4f{0, 0, 0, 0};
   skinny_mma<KIND, MB, NB, DEPTH, SB>(lds, wp, sp, ap, am, K, 0, K, acc);
 
-  // epilogue operands (output rows 4g+q of each block, this lane's column),
-  // fetched after the main loop so that they hold no registers during it
-  int rid[MB][4];
-  float sav[MB][4];
+  // epilogue operands (the core's output layout: lane (r, g) holds row
+  // i*16 + r of each row block and 4 consecutive columns 4g..4g+3 of each
+  // column block), fetched after the main loop so that they hold no
+  // registers during it
+  int rid[MB];
+  float sav[MB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < MB; ++i) {
+    const int rr = p.rows[rbeg + min(i * 16 + r, nrows - 1)];
+    rid[i] = rr;
+    sav[i] = W4 ? 1.0f : p.sa[GATEUP ? rr / p.topk : rr];
+  }
+  // whole 4-column pieces of aligned rows are stored at once (16 bytes of
+  // fp32, 8 of bf16)
+  const bool vec = (p.nout & 3) == 0 && ((uintptr_t)p.out & (W4 && GATEUP ? 7u : 15u)) == 0;
+  if constexpr (GATEUP) {
+    const int col = c0 + 4 * g;
+    float swg[4], swu[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int rr = p.rows[rbeg + min(i * 16 + 4 * g + q, nrows - 1)];
-      rid[i][q] = rr;
-      sav[i][q] = W4 ? 1.0f : p.sa[GATEUP ? rr / p.topk : rr];
+      const int colc = min(col + q, p.nout - 1);
+      swg[q] = W4 ? 1.0f : p.sw[(size_t)e * wrows + colc];
+      swu[q] = W4 ? 1.0f : p.sw[(size_t)e * wrows + p.nout + colc];
     }
-  if constexpr (GATEUP) {
-    const int col = c0 + r, colc = min(col, p.nout - 1);
-    const float swg = W4 ? 1.0f : p.sw[(size_t)e * wrows + colc];
-    const float swu = W4 ? 1.0f : p.sw[(size_t)e * wrows + p.nout + colc];
-    if (col < p.nout) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i) {
+      if (i * 16 + r >= nrows) continue;
+      float av[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float gv, uv;
+        if constexpr (W4) {
+          gv = acc[i][0][q];
+          uv = acc[i][1][q];
+        } else {
+          gv = (acc[i][0][q] * sav[i]) * swg[q];
+          uv = (acc[i][1][q] * sav[i]) * swu[q];
+        }
+        av[q] = moe_activation(p.act, gv, uv);
+      }
+      const size_t o = (size_t)rid[i] * p.nout + col;
+      if (vec && col + 3 < p.nout) {
+        if constexpr (W4)
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + o) =
+              make_uint2(f32_bf16_rne(av[0]) | (f32_bf16_rne(av[1]) << 16),
+                         f32_bf16_rne(av[2]) | (f32_bf16_rne(av[3]) << 16));
+        else
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) = make_float4(av[0], av[1], av[2], av[3]);
+      } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (i * 16 + 4 * g + q < nrows) {
-            float gv, uv;
-            if constexpr (W4) {
-              gv = acc[i][0][q];
-              uv = acc[i][1][q];
-            } else {
-              gv = (acc[i][0][q] * sav[i][q]) * swg;
-              uv = (acc[i][1][q] * sav[i][q]) * swu;
-            }
-            const float av = moe_activation(p.act, gv, uv);
-            const size_t o = (size_t)rid[i][q] * p.nout + col;
-            if constexpr (W4) reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_bf16_rne(av);
-            else reinterpret_cast<float*>(p.out)[o] = av;
+          if (col + q < p.nout) {
+            if constexpr (W4) reinterpret_cast<uint16_t*>(p.out)[o + q] = (uint16_t)f32_bf16_rne(av[q]);
+            else reinterpret_cast<float*>(p.out)[o + q] = av[q];
           }
         }
+      }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int col = c0 + 16 * j + r;
-      const float sw = W4 ? 1.0f : p.sw[(size_t)e * wrows + min(col, p.nout - 1)];
-      if (col < p.nout) {
+      const int col = c0 + 16 * j + 4 * g;
+      float sw[4];
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+      for (int q = 0; q < 4; ++q) sw[q] = W4 ? 1.0f : p.sw[(size_t)e * wrows + min(col + q, p.nout - 1)];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if (i * 16 + r >= nrows) continue;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = W4 ? acc[i][j][q] : (acc[i][j][q] * sav[i]) * sw[q];
+        const size_t o = (size_t)rid[i] * p.nout + col;
+        if (vec && col + 3 < p.nout) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (i * 16 + 4 * g + q < nrows) {
-              const float v = W4 ? acc[i][j][q] : (acc[i][j][q] * sav[i][q]) * sw;
-              reinterpret_cast<float*>(p.out)[(size_t)rid[i][q] * p.nout + col] = v;
-            }
+            if (col + q < p.nout) reinterpret_cast<float*>(p.out)[o + q] = v[q];
+        }
       }
     }
   }

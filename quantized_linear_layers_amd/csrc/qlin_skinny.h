@@ -39,8 +39,10 @@
 //    keep the unpack between the two, so it covers the LDS latency (K=5120,
 //    N=25600, M=64: 44.8 instead of 46.0 us; K=4096, N=14336, M=64: 32.7
 //    instead of 37.9 us).
-// Output layout (MFMA): acc[mb][j] register i of lane (r, g) is row
-// mb*16 + 4g + i, column 16j + r of the wave's columns.
+// Output layout: the weights are the MFMA's first operand, so acc[mb][j]
+// register i of lane (r, g) is row mb*16 + r, column 16j + 4g + i of the
+// wave's columns: each lane holds 4 consecutive columns of one row, which
+// the epilogues store as one 8- or 16-byte piece.
 #pragma once
 
 #include <type_traits>
@@ -266,7 +268,7 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[mb][j] = mfma_bf16(af[mb], bf[j], acc[mb][j]);
+            for (int j = 0; j < NB; ++j) acc[mb][j] = mfma_bf16(bf[j], af[mb], acc[mb][j]);
         }
       }
     } else {
@@ -284,11 +286,11 @@ __device__ __forceinline__ void skinny_mma(uint8_t* lds, const uint8_t* (&wp)[NB
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           if constexpr (KIND == kGemmFP8) {
-            acc[mb][j] = mfma_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
-                                  __builtin_shufflevector(w0[j], w1[j], 0, 1, 2, 3, 4, 5, 6, 7), acc[mb][j]);
+            acc[mb][j] = mfma_fp8(__builtin_shufflevector(w0[j], w1[j], 0, 1, 2, 3, 4, 5, 6, 7),
+                                  __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), acc[mb][j]);
           } else {
-            acc[mb][j] = mfma_i8(a0, w0[j], acc[mb][j]);
-            acc[mb][j] = mfma_i8(a1, w1[j], acc[mb][j]);
+            acc[mb][j] = mfma_i8(w0[j], a0, acc[mb][j]);
+            acc[mb][j] = mfma_i8(w1[j], a1, acc[mb][j]);
           }
         }
       }
