@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void decode_w4_few_kernel(const W4FewArgs p) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma_bf16(af[mb], bf[j], acc[mb][j]);
+          for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma_bf16(bf[j], af[mb], acc[mb][j]);
       }
     }
   };
@@ -269,18 +269,36 @@ __global__ __launch_bounds__(256) void decode_w4_few_kernel(const W4FewArgs p) {
         for (int j = 0; j < NB; ++j)
           acc[mb][j] = acc[mb][j] + red[(((((qr * NQ + qq) * NC + cg) * MB + mb) * NB + j) * 64) + lane];
   }
+  // the weights are the MFMA's first operand: lane (r, g) holds row r of
+  // each row block and columns 4g..4g+3 of each column block, stored as one
+  // 16-byte (fp32) or 8-byte (bf16) piece when aligned and inside the output
+  const bool vec = (p.N & 3) == 0 && ((uintptr_t)p.y & (p.out_f32 ? 15u : 7u)) == 0;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = 16 * (qr * MB + mb) + r;
+    if (m >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int j = 0; j < NB; ++j) {
+      const int n = n0 + 16 * j + 4 * g;
+      const v4f v = acc[mb][j];
+      const size_t o = (size_t)m * p.N + n;
+      if (vec && n + 3 < p.N) {
+        if (p.out_f32)
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + o) = make_float4(v[0], v[1], v[2], v[3]);
+        else
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.y) + o) =
+              make_uint2(f32_bf16_rne(v[0]) | (f32_bf16_rne(v[1]) << 16), f32_bf16_rne(v[2]) | (f32_bf16_rne(v[3]) << 16));
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * (qr * MB + mb) + 4 * g + i, n = n0 + 16 * j + r;
-        if (m < p.M && n < p.N) {
-          if (p.out_f32) reinterpret_cast<float*>(p.y)[(size_t)m * p.N + n] = acc[mb][j][i];
-          else reinterpret_cast<uint16_t*>(p.y)[(size_t)m * p.N + n] = (uint16_t)f32_bf16_rne(acc[mb][j][i]);
+        for (int i = 0; i < 4; ++i) {
+          if (n + i < p.N) {
+            if (p.out_f32) reinterpret_cast<float*>(p.y)[o + i] = v[i];
+            else reinterpret_cast<uint16_t*>(p.y)[o + i] = (uint16_t)f32_bf16_rne(v[i]);
+          }
         }
       }
+    }
+  }
 }
 
 // Compute units of the current device (queried once).
