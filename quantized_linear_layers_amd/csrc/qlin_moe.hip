@@ -193,7 +193,7 @@ template <bool GATEUP>
 constexpr int moe_cols_per_wg() { return GATEUP ? 64 : 128; }
 
 template <int KIND, bool GATEUP, int MB, bool SB>
-__device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int e, int rbeg, int nrows) {
+__device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int tile, int e, int rbeg, int nrows) {
   constexpr bool W4 = KIND == kGemmW4;
   constexpr int ESZ = W4 ? 2 : 1;
   constexpr int NB = 2;
@@ -204,7 +204,7 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int K = p.K;
-  const int c0 = blockIdx.x * moe_cols_per_wg<GATEUP>() + wave * CW;  // this wave's first output column
+  const int c0 = tile * moe_cols_per_wg<GATEUP>() + wave * CW;  // this wave's first output column
   const size_t wrows = GATEUP ? 2 * (size_t)p.nout : (size_t)p.nout;
   const size_t wrow_bytes = W4 ? (size_t)K / 2 : (size_t)K;
   const uint8_t* wbase = p.W + (size_t)e * wrows * wrow_bytes;
@@ -331,21 +331,30 @@ __device__ __forceinline__ void moe_tile(const MoeGemmArgs& p, uint8_t* lds, int
 // (one pass of the weights per block). MBMAX is chosen per call from the
 // average number of rows per expert: 2 (32-row blocks) for light loads, 3
 // (48-row blocks) otherwise, so that nearly every expert is served by one
-// pass while the registers still allow two workgroups per CU. The W4A16
-// kernels with 48-row blocks would take ~275 VGPRs (one wave per SIMD);
-// bounding them to 256 (two workgroups per CU, a few spilled registers)
-// makes the C5 W4A16 block ~20 % faster at T = 512.
+// pass while the registers still allow two workgroups per CU (the 48-row
+// W4A16 kernels fit the 256 VGPRs of that bound without spilling).
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup L to XCD
+// L % 8), each with its own L2; when the expert count is a multiple of 8,
+// the k-th workgroup of XCD x takes column tile k % tiles of expert
+// x + 8 * (k / tiles), so all tiles of an expert share one L2 and its
+// gathered activation rows are fetched into one L2 instead of eight.
 template <int KIND, bool GATEUP, int MBMAX, bool SB>
 __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(const MoeGemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[skinny_lds_bytes<KIND, MBMAX, 2, KIND == kGemmW4 ? 2 : 1>()];
-  const int e = blockIdx.y;
+  constexpr int kXcds = 8;
+  int tile = blockIdx.x, e = blockIdx.y;
+  if (gridDim.y % kXcds == 0) {
+    const int L = blockIdx.y * gridDim.x + blockIdx.x, k = L / kXcds;
+    e = L % kXcds + kXcds * (k / gridDim.x);
+    tile = k % gridDim.x;
+  }
   const int beg = p.off[e], n = p.off[e + 1] - beg;
   for (int rb = 0; rb < n; rb += 16 * MBMAX) {
     const int nr = min(16 * MBMAX, n - rb);
     const int mb = (nr + 15) / 16;
-    if (mb == 1) moe_tile<KIND, GATEUP, 1, SB>(p, lds, e, beg + rb, nr);
-    else if (mb == 2 || MBMAX == 2) moe_tile<KIND, GATEUP, 2, SB>(p, lds, e, beg + rb, nr);
-    else moe_tile<KIND, GATEUP, (MBMAX > 2 ? 3 : 2), SB>(p, lds, e, beg + rb, nr);
+    if (mb == 1) moe_tile<KIND, GATEUP, 1, SB>(p, lds, tile, e, beg + rb, nr);
+    else if (mb == 2 || MBMAX == 2) moe_tile<KIND, GATEUP, 2, SB>(p, lds, tile, e, beg + rb, nr);
+    else moe_tile<KIND, GATEUP, (MBMAX > 2 ? 3 : 2), SB>(p, lds, tile, e, beg + rb, nr);
   }
 }
 
