@@ -636,9 +636,9 @@ def vocab_rows(q, torch, gen, iters):
 # ----------------------------------------------------------------------------
 CSRC = os.path.join(ROOT, "quantized_linear_layers_amd", "csrc")
 DECODE_SOURCES = ("qlin_gemm_decode.hip", "qlin_gemm_w4_decode.hip", "qlin_skinny.h", "qlin_device.h",
-                  "qlin_quant.hip", "qlin_abi.hip")
-PREFILL_SOURCES = ("qlin_gemm_prefill.hip", "qlin_device.h", "qlin_quant.hip", "qlin_abi.hip")
-MOE_SOURCES = ("qlin_moe.hip", "qlin_skinny.h", "qlin_device.h", "qlin_quant.hip")
+                  "qlin_quant.hip", "qlin_quant_row.h", "qlin_abi.hip")
+PREFILL_SOURCES = ("qlin_gemm_prefill.hip", "qlin_device.h", "qlin_quant.hip", "qlin_quant_row.h", "qlin_abi.hip")
+MOE_SOURCES = ("qlin_moe.hip", "qlin_skinny.h", "qlin_device.h", "qlin_quant.hip", "qlin_quant_row.h")
 PMC_SOURCES = {"decode": DECODE_SOURCES, "prefill": PREFILL_SOURCES, "moe": MOE_SOURCES}
 TRAFFIC_MD = {"decode": os.path.join(ROOT, "profiles", "decode_gemms_K5120_N25600_K2048_N8192_pmc_counters.md"),
               "prefill": os.path.join(ROOT, "profiles", "prefill_gemms_M8192_pmc_counters.md"),

@@ -4,9 +4,10 @@
 // router stays outside in bf16; vLLM PR #45854 report: the fp8 MoE takes
 // per-token activation and per-output-channel weight scales).
 //
-// Stages (one kernel each; intermediates live in the workspace):
+// Stages (intermediates live in the workspace):
 //   1. per-token FP8 quant of x                    -> xq [T][H], sx [T]
 //   2. routing bookkeeping (one workgroup): rows of each expert
+//      (1 and 2 share one launch below 1024 tokens)
 //   3. grouped gate_up: for every touched expert, its 2I x H FP8 weights are
 //      streamed once for all of its rows; h = (xq.w13^T)*sx*s13, then
 //      act = SiLU(h[:I]) * h[I:] in fp32        -> act [R][I]   (R = T*topk)
@@ -24,6 +25,7 @@
 
 #include "qlin_device.h"
 #include "qlin_internal.h"
+#include "qlin_quant_row.h"
 #include "qlin_skinny.h"
 
 namespace qlin {
@@ -95,16 +97,16 @@ MoeW4Layout moe_w4_layout(int64_t T, int64_t H, int64_t I, int64_t E, int topk) 
 // off[e] = first position of expert e in rows[]; rows[] lists r = t*topk+j.
 // The order of rows inside an expert does not affect any result (every
 // output row is computed from its own activation row only).
-__global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restrict__ ids, int R,
-                                                         int E, int* __restrict__ off,
-                                                         int* __restrict__ rows) {
-  extern __shared__ int sh[];  // cnt[E], cur[E]
+// One workgroup (any size that is a multiple of 64); sh: 2E ints of LDS.
+// The first KEEP ids of each thread stay in registers for the scatter (one
+// global read of them instead of two).
+template <int KEEP>
+__device__ __forceinline__ void moe_route(const int32_t* __restrict__ ids, int R, int E,
+                                          int* __restrict__ off, int* __restrict__ rows, int* sh) {
   int* cnt = sh;
   int* cur = sh + E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
-  // the first kKeep ids of this thread stay in registers for the scatter
-  // (one global read of them instead of two; R <= 4096 is covered)
-  constexpr int kKeep = 4;
+  constexpr int kKeep = KEEP;
   int keep[kKeep];
 #pragma unroll
   for (int i = 0; i < kKeep; ++i) {
@@ -149,6 +151,28 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
     const int e = ids[r];
     if (e >= 0 && e < E) rows[atomicAdd(&cur[e], 1)] = r;
   }
+}
+
+__global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restrict__ ids, int R,
+                                                         int E, int* __restrict__ off,
+                                                         int* __restrict__ rows) {
+  extern __shared__ int sh[];  // cnt[E], cur[E]
+  moe_route<4>(ids, R, E, off, rows, sh);  // 1024 threads: R <= 4096 in registers
+}
+
+// Stages 1 and 2 of the FP8 block in one launch: workgroup 0 does the
+// routing bookkeeping (the longest workgroup, dispatched first), workgroups
+// 1..T quantise one token each (the two share nothing; as separate launches
+// the routing kernel added its own launch to the block's critical path).
+template <int CMAX>
+__global__ __launch_bounds__(kQThreads) void moe_prep_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                             uint8_t* __restrict__ xq, float* __restrict__ sx,
+                                                             const int32_t* __restrict__ ids, int R, int E,
+                                                             int* __restrict__ off, int* __restrict__ rows) {
+  extern __shared__ int sh[];  // routing: cnt[E], cur[E]
+  __shared__ float red[kQThreads / 64];
+  if (blockIdx.x == 0) moe_route<16>(ids, R, E, off, rows, sh);  // R <= 4096 in registers
+  else quant_row<QLIN_E4M3, CMAX>(x, H, H, xq, sx, (int64_t)blockIdx.x - 1, red);
 }
 
 // ---------------------------------------------------------------- grouped GEMM
@@ -415,9 +439,25 @@ int launch_moe_fp8(const uint16_t* x, int64_t T, int64_t H, int64_t I, int64_t E
   int* rows = reinterpret_cast<int*>(base + L.rows);
   const int R = (int)(T * topk);
 
-  int rc = launch_quant_act(x, T, H, H, QLIN_E4M3, xq, sx, st);
-  if (rc) return rc;
-  moe_route_kernel<<<1, 1024, 2 * E * sizeof(int), st>>>(ids, R, (int)E, off, rows);
+  // token quantisation and routing in one launch where the quantiser takes
+  // a workgroup per token (fewer than 1024 tokens of at most 16384
+  // elements, as launch_quant_act would)
+  int rc = QLIN_OK;
+  const int64_t chunks = H / 8;
+  const dim3 pgrid((unsigned)(T + 1));
+  const size_t psh = 2 * E * sizeof(int);
+  if (T < 1024 && chunks <= 1 * kQThreads)
+    moe_prep_kernel<1><<<pgrid, kQThreads, psh, st>>>(x, (int)T, (int)H, xq, sx, ids, R, (int)E, off, rows);
+  else if (T < 1024 && chunks <= 2 * kQThreads)
+    moe_prep_kernel<2><<<pgrid, kQThreads, psh, st>>>(x, (int)T, (int)H, xq, sx, ids, R, (int)E, off, rows);
+  else if (T < 1024 && chunks <= 4 * kQThreads)
+    moe_prep_kernel<4><<<pgrid, kQThreads, psh, st>>>(x, (int)T, (int)H, xq, sx, ids, R, (int)E, off, rows);
+  else if (T < 1024 && chunks <= 8 * kQThreads)
+    moe_prep_kernel<8><<<pgrid, kQThreads, psh, st>>>(x, (int)T, (int)H, xq, sx, ids, R, (int)E, off, rows);
+  else {
+    if ((rc = launch_quant_act(x, T, H, H, QLIN_E4M3, xq, sx, st))) return rc;
+    moe_route_kernel<<<1, 1024, psh, st>>>(ids, R, (int)E, off, rows);
+  }
   if ((rc = launch_status())) return rc;
 
   // row blocks of 32 rows when an expert averages at most 8 routed rows,

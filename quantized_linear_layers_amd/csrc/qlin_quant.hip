@@ -8,148 +8,17 @@
 // elements), reduced to its absmax, then encoded and written.
 #include "qlin_device.h"
 #include "qlin_internal.h"
+#include "qlin_quant_row.h"
 
 namespace qlin {
 
-constexpr int kQThreads = 256;
-
-// 8 fp32 values -> 8 code bytes (two 32-bit words).
-template <int FMT>
-__device__ __forceinline__ uint2 encode8(const float (&v)[8]) {
-  uint32_t w[2];
-  if (FMT == QLIN_E4M3) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      w[h] = fp8_encode_hw2(v[4 * h], v[4 * h + 1]) | (fp8_encode_hw2(v[4 * h + 2], v[4 * h + 3]) << 16);
-  } else {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      w[h] = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t b = FMT == QLIN_INT8 ? ((uint32_t)int8_code(v[4 * h + i]) & 0xFFu)
-                                      : fp8_encode<true>(v[4 * h + i]);
-        w[h] |= b << (8 * i);
-      }
-    }
-  }
-  return make_uint2(w[0], w[1]);
-}
-
-// a / s for every value a of a bf16 row whose scale is s = absmax / FMAX
-// (absmax a bf16 value, s > 0): the reciprocal quotient with one fused
-// multiply-add correction (Markstein's correction of a reciprocal quotient:
-// q0 = a*y with y = RN(1/s), r = a - q0*s by an fma, q = q0 + r*y by an
-// fma), with a's sign copied onto q so that a zero keeps its sign. For
-// s >= 2^-100 it is the IEEE quotient bit for bit wherever either is at
-// least 2^-12 in magnitude, and below that both encode to a zero of a's
-// sign in every format: an exhaustive check over every positive finite bf16
-// absmax, FMAX 448, 240 and 127, and every bf16 a with |a| <= absmax shows it
-// (3.1e9 pairs). Rows of a smaller scale, where the remainder can fall among
-// the fp32 subnormals, divide.
-struct RowScale {
-  float s, y;
-  bool fast;
-};
-__device__ __forceinline__ RowScale row_scale(float sc) {
-  RowScale r;
-  r.s = sc;
-  r.y = 1.0f / sc;
-  r.fast = sc >= 0x1p-100f && __builtin_isfinite(r.y);
-  return r;
-}
-__device__ __forceinline__ void divide8(float (&v)[8], const RowScale& rs) {
-  if (rs.fast) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float q0 = v[i] * rs.y;
-      v[i] = copysignf(fmaf(fmaf(-q0, rs.s, v[i]), rs.y, q0), v[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = v[i] / rs.s;
-  }
-}
-
-__device__ __forceinline__ void unpack_bf16x8(const uint4& x, float (&v)[8]) {
-  const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(xs[i] << 16);
-    v[2 * i + 1] = __uint_as_float(xs[i] & 0xFFFF0000u);
-  }
-}
-
-// CMAX > 0: the row (K/8 chunks of 8 bf16) is held in registers, CMAX chunks
-// per lane. CMAX == 0: two passes over global memory (rows longer than
-// 16384 elements).
 template <int FMT, int CMAX>
 __global__ __launch_bounds__(kQThreads) void quant_act_kernel(const uint16_t* __restrict__ a,
                                                               int64_t K, int64_t lda,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ s) {
   __shared__ float red[kQThreads / 64];
-  const int64_t m = blockIdx.x;
-  const uint16_t* row = a + m * lda;
-  uint8_t* qrow = q + m * K;
-  const int chunks = (int)(K / 8);
-  constexpr float kFmax = FMT == QLIN_INT8 ? 127.0f : (FMT == QLIN_E4M3FNUZ ? 240.0f : 448.0f);
-  float amax = 0.0f;
-  if (CMAX > 0) {
-    uint4 cache[CMAX > 0 ? CMAX : 1];
-#pragma unroll
-    for (int c = 0; c < CMAX; ++c) {
-      const int idx = threadIdx.x + c * kQThreads;
-      // rows above 8192 elements stream nontemporally (read once; K=14336,
-      // M=8192: 58.7 instead of 65.7 us); shorter ones measured slower so
-      // (K=4096: 20.7 instead of 17.4 us)
-      const uint16_t* src = row + (int64_t)idx * 8;
-      cache[c] = idx < chunks ? (CMAX >= 8 ? ldg16_nt(src) : ldg16(src)) : make_uint4(0, 0, 0, 0);
-      float v[8];
-      unpack_bf16x8(cache[c], v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    }
-    amax = block_max<kQThreads / 64>(amax, red);
-    const float sc = amax > 0.0f ? amax / kFmax : 0.0f;
-    const RowScale rs = row_scale(sc);
-#pragma unroll
-    for (int c = 0; c < CMAX; ++c) {
-      const int idx = threadIdx.x + c * kQThreads;
-      if (idx < chunks) {
-        uint2 out = make_uint2(0, 0);
-        if (sc > 0.0f) {
-          float v[8];
-          unpack_bf16x8(cache[c], v);
-          divide8(v, rs);
-          out = encode8<FMT>(v);
-        }
-        *reinterpret_cast<uint2*>(qrow + (int64_t)idx * 8) = out;
-      }
-    }
-    if (threadIdx.x == 0) s[m] = sc;
-  } else {
-    for (int idx = threadIdx.x; idx < chunks; idx += kQThreads) {
-      float v[8];
-      unpack_bf16x8(ldg16(row + (int64_t)idx * 8), v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    }
-    amax = block_max<kQThreads / 64>(amax, red);
-    const float sc = amax > 0.0f ? amax / kFmax : 0.0f;
-    const RowScale rs = row_scale(sc);
-    for (int idx = threadIdx.x; idx < chunks; idx += kQThreads) {
-      uint2 out = make_uint2(0, 0);
-      if (sc > 0.0f) {
-        float v[8];
-        unpack_bf16x8(ldg16(row + (int64_t)idx * 8), v);
-        divide8(v, rs);
-        out = encode8<FMT>(v);
-      }
-      *reinterpret_cast<uint2*>(qrow + (int64_t)idx * 8) = out;
-    }
-    if (threadIdx.x == 0) s[m] = sc;
-  }
+  quant_row<FMT, CMAX>(a, K, lda, q, s, blockIdx.x, red);
 }
 
 // Rows of at most 2048 elements: one wave per row (four rows per
@@ -272,9 +141,64 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_f32_kernel(const float* 
   if (threadIdx.x == 0) s[m] = sc;
 }
 
+// Rows of at most 64*8*CPL fp32 values (the MoE intermediate, I = 768): one
+// wave per row (four rows per workgroup), CPL chunks of 8 per lane held in
+// registers, the absmax reduced within the wave; the same scale, division
+// and encoder as above. A workgroup per row left 160 of its 256 threads idle
+// at I = 768 and read each row twice (T = 512: 4096 rows).
+template <int CPL>
+__global__ __launch_bounds__(256) void quant_rows_f32_wave_kernel(const float* __restrict__ a, int64_t M,
+                                                                  int64_t K, uint8_t* __restrict__ q,
+                                                                  float* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;  // whole waves leave together
+  const float* row = a + m * K;
+  const int chunks = (int)(K / 8);
+  float4 x[CPL][2];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int idx = lane + 64 * c;
+    const bool in = idx < chunks;
+    x[c][0] = in ? *reinterpret_cast<const float4*>(row + (int64_t)idx * 8) : make_float4(0, 0, 0, 0);
+    x[c][1] = in ? *reinterpret_cast<const float4*>(row + (int64_t)idx * 8 + 4) : make_float4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[c][h].x), fabsf(x[c][h].y)), fmaxf(fabsf(x[c][h].z), fabsf(x[c][h].w))));
+  amax = wave_max(amax);
+  const float sc = amax > 0.0f ? amax / 448.0f : 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < chunks) {
+      uint2 out = make_uint2(0, 0);
+      if (sc > 0.0f) {
+        float v[8] = {x[c][0].x / sc, x[c][0].y / sc, x[c][0].z / sc, x[c][0].w / sc,
+                      x[c][1].x / sc, x[c][1].y / sc, x[c][1].z / sc, x[c][1].w / sc};
+        out = encode8<QLIN_E4M3>(v);
+      }
+      *reinterpret_cast<uint2*>(q + m * K + (int64_t)idx * 8) = out;
+    }
+  }
+  if (lane == 0) s[m] = sc;
+}
+
 int launch_quant_rows_f32(const float* a, int64_t M, int64_t K, uint8_t* q, float* s,
                           hipStream_t st) {
-  quant_rows_f32_kernel<<<dim3((unsigned)M), kQThreads, 0, st>>>(a, K, q, s);
+  const int64_t chunks = K / 8;
+  const dim3 wgrid((unsigned)((M + 3) / 4));
+  if (chunks <= 64)
+    quant_rows_f32_wave_kernel<1><<<wgrid, 256, 0, st>>>(a, M, K, q, s);
+  else if (chunks <= 128)
+    quant_rows_f32_wave_kernel<2><<<wgrid, 256, 0, st>>>(a, M, K, q, s);
+  else if (chunks <= 256)
+    quant_rows_f32_wave_kernel<4><<<wgrid, 256, 0, st>>>(a, M, K, q, s);
+  else
+    quant_rows_f32_kernel<<<dim3((unsigned)M), kQThreads, 0, st>>>(a, K, q, s);
   return launch_status();
 }
 

@@ -778,6 +778,16 @@ def test_moe_degenerate_shapes(q, oracle):
     assert not y.any()
 
 
+@pytest.mark.parametrize("I", [32, 512, 1056, 2080])
+def test_moe_requant_row_lengths(q, oracle, I):
+    """The fp32 intermediate's requantisation at every row-length path: a
+    wave per row holding 1, 2 or 4 chunks of 8 per lane (I = 32 and 512,
+    768 in the C5 blocks, 1056) and a workgroup per row above 2048 (2080);
+    each stage as in the other FP8 MoE tests, the requantisation bit-exact."""
+    d = gen.moe_config(E=4, H=64, I=I, T=5, topk=2, seed=73)
+    _moe_check(q, oracle, d, _moe_weights(oracle, d))
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "int8", "w4a16"])
 def test_gemm_smallest_shapes(q, oracle, fmt):
     """N = 16 and K = 32 (one int4 group; the weights of every format come
