@@ -123,16 +123,19 @@ __global__ __launch_bounds__(256) void decode_w4_few_kernel(const W4FewArgs p) {
     row = (x >> 5) / CK % MR;
     part = (x >> 5) / CK / MR;
   };
+  // Rows >= M are staged from row M - 1 (valid memory) and never read (their
+  // lanes read the zero row): no divergent branch per piece, which had cost
+  // each load and each LDS write an exec-mask save, branch and restore.
   auto aload = [&](int rd) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       const int x = tid + 256 * e;
       int part, row, cu, pc;
       apiece(x, part, row, cu, pc);
-      if (x < kPieces && row < p.M) {
+      if (kPieces % 256 == 0 || x < kPieces) {
         // clamp past the part's units or K (read valid memory; never used)
         const int u = min(part * p.kq + min(rd * CK + cu, p.kq - 1), units - 1);
-        areg[e] = ldg16(p.A + (size_t)row * p.lda + (size_t)u * 256 + pc * 8);
+        areg[e] = ldg16(p.A + (size_t)min(row, p.M - 1) * p.lda + (size_t)u * 256 + pc * 8);
       }
     }
   };
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(256) void decode_w4_few_kernel(const W4FewArgs p) {
       const int x = tid + 256 * e;
       int part, row, cu, pc;
       apiece(x, part, row, cu, pc);
-      if (x < kPieces && row < p.M)
+      if (kPieces % 256 == 0 || x < kPieces)
         *reinterpret_cast<uint4*>(lds + (buf * NQ + part) * kPartBuf + row * RS + cu * 512 + pc * 16) = areg[e];
     }
   };
