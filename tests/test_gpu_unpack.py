@@ -113,7 +113,7 @@ def run_decode(q, oracle, N, K, Ms, misalign=False, extra_m1=()):
 DECODE_CASES = [
     # id, N, K, Ms, misalign, M=1 rows
     ("small_layer_one_unit", 7808, 256, (16,), False, (0, 1, 131, 255)),
-    ("small_layer_k_parts", 1952, 1024, (1, 4, 8, 16), False, ()),
+    ("small_layer_k_parts", 1952, 1024, (1, 3, 4, 5, 8, 12, 16), False, ()),
     ("small_layer_unaligned_steps", 7808, 256, (16,), True, (3,)),
     ("small_layer_32_64_rows", 8192, 512, (32, 48, 64), False, (0, 300)),
     ("small_layer_64_rows_one_part", 8160, 256, (17, 64), False, ()),
