@@ -778,6 +778,16 @@ def test_moe_degenerate_shapes(q, oracle):
     assert not y.any()
 
 
+@pytest.mark.parametrize("T, topk", [(600, 8), (1030, 2)], ids=["fused_prep_r4800", "separate_launches_t1030"])
+def test_moe_token_counts(q, oracle, T, topk):
+    """The FP8 block's first stage at both launch shapes: below 1024 tokens
+    one launch quantises the tokens and routes (here 4800 routed rows, more
+    than the routing workgroup keeps in registers); from 1024 tokens the
+    quantiser and the routing kernel run as two launches."""
+    d = gen.moe_config(E=16, H=64, I=32, T=T, topk=topk, seed=74)
+    _moe_check(q, oracle, d, _moe_weights(oracle, d))
+
+
 @pytest.mark.parametrize("I", [32, 512, 1056, 2080])
 def test_moe_requant_row_lengths(q, oracle, I):
     """The fp32 intermediate's requantisation at every row-length path: a
