@@ -315,28 +315,38 @@ static int decode_cus() {
   return cus;
 }
 
-// Grid: 16*NB*NW columns per workgroup, S splits of K. A wave takes one
-// 16-column block, or two when the 128-column tiles alone reach about three
-// quarters of the CUs (fp8/int8 at any M: more bytes in flight per wave,
-// K=5120, N=25600: 22.7 instead of 23.6 us at M = 1; W4A16 from MB = 3,
-// where it halves the activation fragments read per weight byte; at M <= 16
-// it was slower). Split-K costs a write and a read of S*M*N partial
+// Grid: 16*NB*NW columns per workgroup, S splits of K. On a wide layer (the
+// 128-column tiles alone reach about three quarters of the CUs) an
+// fp8/int8 wave takes two 16-column blocks (more bytes in flight per wave,
+// K=5120, N=25600: 22.7 instead of 23.6 us at M = 1). A W4A16 layer whose
+// 128-column tiles number between 3/4 and twice the CUs runs 8 waves of
+// one block each (two waves per SIMD: one wave's unpack hides the other's
+// waits) over the whole K range, with no split (K=5120, N=25600: M = 64
+// 41.8 us, M = 48 35.3, M = 32 29.7, M = 8 22.3, against 46.2 / 40.3 / 37.6
+// / 22.8 for two blocks per wave with 2 splits above 32 rows and one block
+// with 4 waves below; N=32768, K=4096, M = 64: 39.5 against 42.5); on wider
+// ones (the K=1536, N=262144 lm_head: M = 64 121 against 101 us) two blocks
+// per wave with 8 waves from 33 rows, one block with 4 waves below.
+// Split-K costs a write and a read of S*M*N partial
 // sums and a second, serial phase, so fp8/int8 split only when the column
 // tiles reach fewer than half the CUs (K=2048, N=8192, 128 tiles: M = 1
-// 5.5 us unsplit, 6.2 us in 2 splits); W4A16, bound by its unpack and MFMA
-// issue rather than by HBM, splits to about three quarters of the CUs, and
-// with one block above 16 rows to two workgroups per CU. Each split keeps
-// >= 4 steps of 128 K.
+// 5.5 us unsplit, 6.2 us in 2 splits); W4A16 on narrower layers, bound by
+// its unpack and MFMA issue rather than by HBM, splits to about three
+// quarters of the CUs, and with one block above 16 rows to two workgroups
+// per CU. Each split keeps >= 4 steps of 128 K.
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   const int64_t cus = decode_cus();
   c.MB = (int)((M + 15) / 16);
-  c.NB = (kind != kGemmW4 || c.MB >= 3) && (N + 127) / 128 >= 3 * cus / 4 ? 2 : 1;
+  const int64_t t128 = (N + 127) / 128;
+  const bool wide = t128 >= 3 * cus / 4;
+  const bool w4full = kind == kGemmW4 && wide && t128 < 2 * cus;  // 8 waves, one block, whole K
+  c.NB = (kind != kGemmW4 || (c.MB >= 3 && !w4full)) && wide ? 2 : 1;
   // fp8/int8 at M <= 16 with one block per wave: 2 waves per workgroup, so
   // the same waves spread over twice the CUs (K=2048, N=8192: M = 1 5.5 ->
   // 5.3 us, M = 8 6.1 -> 5.7 us; 1 wave per workgroup was slower, and at
   // M = 64 2 waves gained nothing)
-  c.NW = kind == kGemmW4 && c.NB == 2 ? 8 : kind != kGemmW4 && c.MB == 1 && c.NB == 1 ? 2 : 4;
+  c.NW = kind == kGemmW4 && (w4full || c.NB == 2) ? 8 : kind != kGemmW4 && c.MB == 1 && c.NB == 1 ? 2 : 4;
   // W4A16 at M <= 16 on a layer too narrow for the column tiles to fill the
   // device: the 4 waves of a workgroup split K instead of the grid (one
   // block each; K=2048, N=8192, M = 1: 5.9 instead of 6.9 us with 2 global
@@ -347,7 +357,7 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
   const int64_t want = kind != kGemmW4 ? cus / 2 : c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
-  int64_t S = (want + c.tiles - 1) / c.tiles;
+  int64_t S = w4full ? 1 : (want + c.tiles - 1) / c.tiles;
   S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
   if (c.tiles > (int)(kGemmCounterBytes / 4)) S = 1;  // one counter per tile; such grids need no split
   int64_t steps_per = (ksteps + S - 1) / S;
@@ -357,39 +367,58 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   return c;
 }
 
-// Dispatch on (kind, MB, NB, bulk steps) to the instantiation that serves
-// it. DEPTH (weight units in flight per wave), as measured: 4 fp8/int8
-// 128-K units (8 was slower); int4 256-K units: 2 at MB = 1 and with two
-// blocks (register bound), 4 otherwise. W4A16 with two blocks per wave runs
-// 8 waves per workgroup (two per SIMD: one wave's unpack hides the other's
-// waits; K=5120, N=25600, M=64: 43.7 instead of 52.4 us; with one block
-// per wave, or fp8/int8, 8 waves measured no better).
+// Dispatch on (kind, MB, NB, waves, bulk steps) to the instantiation that
+// serves it. DEPTH (weight units in flight per wave), as measured: 4
+// fp8/int8 128-K units (8 was slower); int4 256-K units: 2 at MB = 1 and
+// with two blocks (register bound), 4 otherwise.
 template <typename F>
-static auto with_decode_inst(int kind, int MB, int NB, bool wk, bool sb, F&& f) {
-#define QLIN_DEC(K, D1, D2, D22, NW2, SB)                                                          \
-  switch (MB) {                                                                              \
-    case 1:                                                                                  \
-      if constexpr (K == kGemmW4) if (wk) return f.template operator()<K, 1, 1, D1, SB, 4, true>(); \
-      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 1, 2, D2, SB, 4, false>(); \
-      return f.template operator()<K, 1, 1, D1, SB, K == kGemmW4 ? 4 : 2, false>();          \
-    case 2:                                                                                  \
-      if constexpr (K != kGemmW4) if (NB == 2) return f.template operator()<K, 2, 2, D2, SB, 4, false>(); \
-      return f.template operator()<K, 2, 1, D2, SB, 4, false>();                             \
-    case 3: return NB == 2 ? f.template operator()<K, 3, 2, D22, SB, NW2, false>() : f.template operator()<K, 3, 1, D2, SB, 4, false>(); \
-    default: return NB == 2 ? f.template operator()<K, 4, 2, D22, SB, NW2, false>() : f.template operator()<K, 4, 1, D2, SB, 4, false>(); \
+static auto with_decode_inst(int kind, int MB, int NB, int NW, bool wk, bool sb, F&& f) {
+#define QLIN_DEC_W4(SB)                                                                       \
+  switch (MB) {                                                                               \
+    case 1:                                                                                   \
+      if (wk) return f.template operator()<kGemmW4, 1, 1, 2, SB, 4, true>();                  \
+      if (NW == 8) return f.template operator()<kGemmW4, 1, 1, 2, SB, 8, false>();           \
+      return f.template operator()<kGemmW4, 1, 1, 2, SB, 4, false>();                         \
+    case 2:                                                                                   \
+      if (NW == 8) return f.template operator()<kGemmW4, 2, 1, 4, SB, 8, false>();           \
+      return f.template operator()<kGemmW4, 2, 1, 4, SB, 4, false>();                         \
+    case 3:                                                                                   \
+      if (NB == 2) return f.template operator()<kGemmW4, 3, 2, 2, SB, 8, false>();           \
+      if (NW == 8) return f.template operator()<kGemmW4, 3, 1, 4, SB, 8, false>();           \
+      return f.template operator()<kGemmW4, 3, 1, 4, SB, 4, false>();                         \
+    default:                                                                                  \
+      if (NB == 2) return f.template operator()<kGemmW4, 4, 2, 2, SB, 8, false>();           \
+      if (NW == 8) return f.template operator()<kGemmW4, 4, 1, 4, SB, 8, false>();           \
+      return f.template operator()<kGemmW4, 4, 1, 4, SB, 4, false>();                         \
+  }
+#define QLIN_DEC_8(K)                                                                         \
+  switch (MB) {                                                                               \
+    case 1:                                                                                   \
+      if (NB == 2) return f.template operator()<K, 1, 2, 4, false, 4, false>();              \
+      return f.template operator()<K, 1, 1, 4, false, 2, false>();                            \
+    case 2:                                                                                   \
+      if (NB == 2) return f.template operator()<K, 2, 2, 4, false, 4, false>();              \
+      return f.template operator()<K, 2, 1, 4, false, 4, false>();                            \
+    case 3:                                                                                   \
+      if (NB == 2) return f.template operator()<K, 3, 2, 4, false, 4, false>();              \
+      return f.template operator()<K, 3, 1, 4, false, 4, false>();                            \
+    default:                                                                                  \
+      if (NB == 2) return f.template operator()<K, 4, 2, 4, false, 4, false>();              \
+      return f.template operator()<K, 4, 1, 4, false, 4, false>();                            \
   }
   if (kind == kGemmW4) {
     if (sb) {
-      QLIN_DEC(kGemmW4, 2, 4, 2, 8, true)
+      QLIN_DEC_W4(true)
     } else {
-      QLIN_DEC(kGemmW4, 2, 4, 2, 8, false)
+      QLIN_DEC_W4(false)
     }
   } else if (kind == kGemmI8) {
-    QLIN_DEC(kGemmI8, 4, 4, 4, 4, false)
+    QLIN_DEC_8(kGemmI8)
   } else {
-    QLIN_DEC(kGemmFP8, 4, 4, 4, 4, false)
+    QLIN_DEC_8(kGemmFP8)
   }
-#undef QLIN_DEC
+#undef QLIN_DEC_W4
+#undef QLIN_DEC_8
 }
 
 // Workspace of a split-K call: a fixed counter area (one word per column
@@ -442,7 +471,7 @@ int launch_decode(int kind, const void* a, int64_t lda, const float* sa, const v
   }
   // int4 steps in 16-byte pieces of 8 groups: aligned rows, whole pieces
   const bool sb = kind == kGemmW4 && K % 256 == 0 && ((uintptr_t)wsc & 15) == 0;
-  with_decode_inst(kind, c.MB, c.NB, c.WK, sb, LaunchFn{&g, &c, st});
+  with_decode_inst(kind, c.MB, c.NB, c.NW, c.WK, sb, LaunchFn{&g, &c, st});
   return launch_status();
 }
 

@@ -257,8 +257,8 @@ def test_gemm_full_outputs(q, oracle, fmt, case):
 
 
 def test_gemm_w4a16_wide_ragged_k(q, oracle):
-    """N wide enough for two column blocks per wave (8 waves per workgroup
-    for W4A16) with K % 256 != 0 (per-unit step loads), M = 40 and 64."""
+    """N wide enough for the W4A16 8-wave workgroups over the whole K range
+    with K % 256 != 0 (per-unit step loads), M = 40 and 64."""
     d = gen.linear_config(1, n=24576, k=288, m=64)
     ops = _operands(oracle, d, "w4a16")
     for M in (40, 64):

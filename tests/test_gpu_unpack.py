@@ -107,9 +107,10 @@ def run_decode(q, oracle, N, K, Ms, misalign=False, extra_m1=()):
 # 32 or 64 staged rows). Otherwise the streaming core: one
 # 16-row block (M <= 16) on a layer of at most 12224 columns splits K over
 # the 4 waves of a workgroup (WK); wider layers give each wave its own
-# columns; M = 33..64 on a layer of at least 24449 columns runs two column
-# blocks per wave in 8-wave workgroups. K % 256 == 0 with 16-byte aligned
-# step rows loads the steps in bulk, otherwise per unit.
+# columns; a layer of 24449..65536 columns runs 8-wave workgroups over the
+# whole K range at every M, a wider one two column blocks per wave in 8-wave
+# workgroups at M = 33..64. K % 256 == 0 with 16-byte aligned step rows
+# loads the steps in bulk, otherwise per unit.
 DECODE_CASES = [
     # id, N, K, Ms, misalign, M=1 rows
     ("small_layer_one_unit", 7808, 256, (16,), False, (0, 1, 131, 255)),
@@ -122,8 +123,11 @@ DECODE_CASES = [
     ("wide_mb1_per_unit", 12288, 288, (16,), False, ()),
     ("mb2_mb3_mb4_bulk", 4096, 512, (32, 48, 64), False, ()),
     ("mb2_mb4_per_unit", 4096, 288, (32, 64), False, ()),
-    ("two_blocks_8_waves_bulk", 24576, 256, (48, 64), False, ()),
-    ("two_blocks_8_waves_per_unit", 24576, 288, (64,), False, ()),
+    ("wide_8_waves_bulk", 24576, 256, (1, 17, 48, 64), False, (0, 255)),
+    ("wide_8_waves_per_unit", 24576, 288, (16, 32, 64), False, ()),
+    ("wide_8_waves_unaligned_steps", 24576, 512, (8, 64), True, ()),
+    ("two_blocks_8_waves_bulk", 65664, 256, (48, 64), False, ()),
+    ("two_blocks_8_waves_per_unit", 65664, 288, (64,), False, ()),
 ]
 
 
