@@ -328,12 +328,15 @@ static int decode_cus() {
 // ones (the K=1536, N=262144 lm_head: M = 64 121 against 101 us) two blocks
 // per wave with 8 waves from 33 rows, one block with 4 waves below.
 // Split-K costs a write and a read of S*M*N partial
-// sums and a second, serial phase, so fp8/int8 split only when the column
-// tiles reach fewer than half the CUs (K=2048, N=8192, 128 tiles: M = 1
-// 5.5 us unsplit, 6.2 us in 2 splits); W4A16 on narrower layers, bound by
-// its unpack and MFMA issue rather than by HBM, splits to about three
-// quarters of the CUs, and with one block above 16 rows to two workgroups
-// per CU. Each split keeps >= 4 steps of 128 K.
+// sums and a second, serial phase. fp8/int8 split when the grid's waves
+// reach fewer than 3/4 of the SIMDs, to about one wave per SIMD, with at
+// least 2048 K per split (512 when the waves reach fewer than half the CUs)
+// (K=14336, N=4096: M = 1 12.7 instead of 21.0 us, M = 8 12.9 instead of
+// 21.1, M = 64 18.1 instead of 24.3, in 4 splits; K=2048, N=8192: 5.5 us
+// unsplit against 6.2 in 2 splits at M = 1, 8.4 against 10.1 at M = 64). W4A16 on narrower layers, bound by its unpack
+// and MFMA issue rather than by HBM, splits to about three quarters of the
+// CUs, and with one block above 16 rows to two workgroups per CU, each split
+// keeping >= 4 steps of 128 K.
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   const int64_t cus = decode_cus();
@@ -356,9 +359,16 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   const int64_t cols = (int64_t)16 * (c.WK ? 1 : c.NW) * c.NB;
   c.tiles = (int)((N + cols - 1) / cols);
   const int64_t ksteps = (K + 127) / 128;
-  const int64_t want = kind != kGemmW4 ? cus / 2 : c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
-  int64_t S = w4full ? 1 : (want + c.tiles - 1) / c.tiles;
-  S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
+  int64_t S;
+  if (kind != kGemmW4) {
+    const int64_t waves = (int64_t)c.tiles * c.NW;
+    S = waves >= 3 * cus ? 1 : (4 * cus + waves - 1) / waves;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / (2 * waves >= cus ? 16 : 4))));
+  } else {
+    const int64_t want = c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
+    S = w4full ? 1 : (want + c.tiles - 1) / c.tiles;
+    S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
+  }
   if (c.tiles > (int)(kGemmCounterBytes / 4)) S = 1;  // one counter per tile; such grids need no split
   int64_t steps_per = (ksteps + S - 1) / S;
   steps_per = (steps_per + 1) / 2 * 2;  // whole 256-K chunks
