@@ -333,10 +333,12 @@ static int decode_cus() {
 // least 2048 K per split (512 when the waves reach fewer than half the CUs)
 // (K=14336, N=4096: M = 1 12.7 instead of 21.0 us, M = 8 12.9 instead of
 // 21.1, M = 64 18.1 instead of 24.3, in 4 splits; K=2048, N=8192: 5.5 us
-// unsplit against 6.2 in 2 splits at M = 1, 8.4 against 10.1 at M = 64). W4A16 on narrower layers, bound by its unpack
-// and MFMA issue rather than by HBM, splits to about three quarters of the
-// CUs, and with one block above 16 rows to two workgroups per CU, each split
-// keeping >= 4 steps of 128 K.
+// unsplit against 6.2 in 2 splits at M = 1, 8.4 against 10.1 at M = 64).
+// W4A16 on narrower layers, bound by its unpack and MFMA issue rather than
+// by HBM, splits to about two workgroups per CU (the nearest count: K=4096,
+// N=14336, M = 64 28.2 us in 2 splits against 32.3 in 3; K=5120, N=16384,
+// M = 8 15.3 in 2 against 16.5 unsplit), each split keeping >= 4 steps of
+// 128 K.
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   const int64_t cus = decode_cus();
@@ -365,8 +367,7 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
     S = waves >= 3 * cus ? 1 : (4 * cus + waves - 1) / waves;
     S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / (2 * waves >= cus ? 16 : 4))));
   } else {
-    const int64_t want = c.MB >= 2 && c.NB == 1 ? 2 * cus : 3 * cus / 4;
-    S = w4full ? 1 : (want + c.tiles - 1) / c.tiles;
+    S = w4full ? 1 : (2 * cus + c.tiles / 2) / c.tiles;
     S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
   }
   if (c.tiles > (int)(kGemmCounterBytes / 4)) S = 1;  // one counter per tile; such grids need no split
