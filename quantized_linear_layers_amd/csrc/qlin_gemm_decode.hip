@@ -318,40 +318,42 @@ static int decode_cus() {
 // Grid: 16*NB*NW columns per workgroup, S splits of K. On a wide layer (the
 // 128-column tiles alone reach about three quarters of the CUs) an
 // fp8/int8 wave takes two 16-column blocks (more bytes in flight per wave,
-// K=5120, N=25600: 22.7 instead of 23.6 us at M = 1). A W4A16 layer whose
-// 128-column tiles number between 3/4 and twice the CUs runs 8 waves of
-// one block each (two waves per SIMD: one wave's unpack hides the other's
-// waits) over the whole K range, with no split (K=5120, N=25600: M = 64
-// 41.8 us, M = 48 35.3, M = 32 29.7, M = 8 22.3, against 46.2 / 40.3 / 37.6
-// / 22.8 for two blocks per wave with 2 splits above 32 rows and one block
-// with 4 waves below; N=32768, K=4096, M = 64: 39.5 against 42.5); on wider
-// ones (the K=1536, N=262144 lm_head: M = 64 121 against 101 us) two blocks
-// per wave with 8 waves from 33 rows, one block with 4 waves below.
-// Split-K costs a write and a read of S*M*N partial
-// sums and a second, serial phase. fp8/int8 split when the grid's waves
-// reach fewer than 3/4 of the SIMDs, to about one wave per SIMD, with at
-// least 2048 K per split (512 when the waves reach fewer than half the CUs)
-// (K=14336, N=4096: M = 1 12.7 instead of 21.0 us, M = 8 12.9 instead of
-// 21.1, M = 64 18.1 instead of 24.3, in 4 splits; K=2048, N=8192: 5.5 us
-// unsplit against 6.2 in 2 splits at M = 1, 8.4 against 10.1 at M = 64).
-// W4A16 on narrower layers, bound by its unpack and MFMA issue rather than
-// by HBM, splits to about two workgroups per CU (the nearest count: K=4096,
-// N=14336, M = 64 28.2 us in 2 splits against 32.3 in 3; K=5120, N=16384,
-// M = 8 15.3 in 2 against 16.5 unsplit), each split keeping >= 4 steps of
-// 128 K.
+// K=5120, N=25600: 22.7 instead of 23.6 us at M = 1). A W4A16 layer of
+// 1/4 to 2x the CUs in 128-column tiles runs 8 waves of one block each
+// (two waves per SIMD: one wave's unpack hides the other's waits; the 8
+// waves share one activation staging), split over K to about one workgroup
+// per CU -- none at K=5120, N=25600 (M = 64 41.8 us, M = 48 35.3, M = 32
+// 29.7, M = 8 22.3, against 46.2 / 40.3 / 37.6 / 22.8 for two blocks per
+// wave with 2 splits above 32 rows and one block with 4 waves and splits
+// below; N=32768, K=4096, M = 64: 39.5 against 42.5), 2 at K=5120,
+// N=16384 (M = 32 20.7 against 22.5 with 4-wave workgroups) and K=4096,
+// N=14336 (M = 64 26.2 against 28.6). Wider W4A16 layers (the K=1536,
+// N=262144 lm_head: M = 64 121 against 101 us) take two blocks per wave
+// with 8 waves from 33 rows, one block with 4 waves below, unsplit;
+// narrower ones one block with 4 waves, split to about two workgroups per
+// CU (K=14336, N=4096, M = 64: 26.9 us against 28.6 with 8 waves).
+// Split-K costs a write and a read of S*M*N partial sums and a second,
+// serial phase. fp8/int8 split when the grid's waves reach fewer than 3/4
+// of the SIMDs, to about one wave per SIMD, with at least 2048 K per split
+// (512 when the waves reach fewer than half the CUs) (K=14336, N=4096: M =
+// 1 12.7 instead of 21.0 us, M = 8 12.9 instead of 21.1, M = 64 18.1
+// instead of 24.3, in 4 splits; K=2048, N=8192: 5.5 us unsplit against 6.2
+// in 2 splits at M = 1, 8.4 against 10.1 at M = 64). The W4A16 wave-private
+// K mode (below) also splits to about two of its 4-wave workgroups per CU.
+// W4A16 splits keep >= 4 steps of 128 K.
 static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
   DecodeCfg c{};
   const int64_t cus = decode_cus();
   c.MB = (int)((M + 15) / 16);
   const int64_t t128 = (N + 127) / 128;
   const bool wide = t128 >= 3 * cus / 4;
-  const bool w4full = kind == kGemmW4 && wide && t128 < 2 * cus;  // 8 waves, one block, whole K
-  c.NB = (kind != kGemmW4 || (c.MB >= 3 && !w4full)) && wide ? 2 : 1;
+  const bool w4eight = kind == kGemmW4 && 4 * t128 >= cus && t128 < 2 * cus;  // 8 waves of one block
+  c.NB = (kind != kGemmW4 || (c.MB >= 3 && !w4eight)) && wide ? 2 : 1;
   // fp8/int8 at M <= 16 with one block per wave: 2 waves per workgroup, so
   // the same waves spread over twice the CUs (K=2048, N=8192: M = 1 5.5 ->
   // 5.3 us, M = 8 6.1 -> 5.7 us; 1 wave per workgroup was slower, and at
   // M = 64 2 waves gained nothing)
-  c.NW = kind == kGemmW4 && (w4full || c.NB == 2) ? 8 : kind != kGemmW4 && c.MB == 1 && c.NB == 1 ? 2 : 4;
+  c.NW = kind == kGemmW4 && (w4eight || c.NB == 2) ? 8 : kind != kGemmW4 && c.MB == 1 && c.NB == 1 ? 2 : 4;
   // W4A16 at M <= 16 on a layer too narrow for the column tiles to fill the
   // device: the 4 waves of a workgroup split K instead of the grid (one
   // block each; K=2048, N=8192, M = 1: 5.9 instead of 6.9 us with 2 global
@@ -367,7 +369,7 @@ static DecodeCfg decode_cfg(int kind, int64_t M, int64_t N, int64_t K) {
     S = waves >= 3 * cus ? 1 : (4 * cus + waves - 1) / waves;
     S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / (2 * waves >= cus ? 16 : 4))));
   } else {
-    S = w4full ? 1 : (2 * cus + c.tiles / 2) / c.tiles;
+    S = ((w4eight ? 1 : 2) * cus + c.tiles / 2) / c.tiles;
     S = std::max<int64_t>(1, std::min<int64_t>(S, std::min<int64_t>(8, ksteps / 4)));
   }
   if (c.tiles > (int)(kGemmCounterBytes / 4)) S = 1;  // one counter per tile; such grids need no split
