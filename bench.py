@@ -647,7 +647,7 @@ COPY_BYTES = 256 << 20
 # kernels the library launches per call (the counter summary assigns
 # dispatches to calls by these counts)
 LINEAR_KERNELS = 2       # per-token quantisation, GEMM
-MOE_FP8_KERNELS = 6      # quantisation, routing, gate_up, requantisation, down, combine
+MOE_FP8_KERNELS = 5      # quantisation with routing, gate_up, requantisation, down, combine
 MOE_W4A16_KERNELS = 4    # routing, gate_up, down, combine
 
 
@@ -849,10 +849,13 @@ def summarize_trace(csv_path, top):
 
 
 def summarize_pmc(dirs, out_md, cmds):
-    """Counter summary of one workload: dispatches after the marker are
-    assigned, in order, to the plan's rows (launches x kernels per call);
-    per row and kernel the median dispatch is kept. FETCH_SIZE / WRITE_SIZE
-    are scaled by what they read for the 256 MiB copy (known bytes)."""
+    """Counter summary of one workload: a row's `launches` calls follow its
+    marker dispatch (then the next row's warm-up call and the next marker);
+    the kernels per call are the planned count when the dispatch names
+    repeat with that period, else the shortest period they repeat with (a
+    call's kernel count can depend on the shape); per row and
+    kernel the median dispatch is kept. FETCH_SIZE / WRITE_SIZE are scaled
+    by what they read for the 256 MiB copy (known bytes)."""
     import statistics
 
     plan_path = None
@@ -881,12 +884,19 @@ def summarize_pmc(dirs, out_md, cmds):
         marks = [i for i, e in enumerate(ds) if "fp8_encode" in e["kernel"]]
         if len(marks) < len(plan["rows"]) + 1:
             raise ValueError(f"{d}: {len(marks)} marker dispatches for {len(plan['rows'])} rows")
-        for (name, kpc, wbytes), m in zip(plan["rows"], marks):
-            i = m + 1
-            seq = ds[i:i + kpc * plan["launches"]]
-            if len(seq) < kpc * plan["launches"] or any("fp8_encode" in e["kernel"] for e in seq):
-                raise ValueError(f"{d}: row {name}: fewer dispatches than planned before the next marker")
-            i += kpc * plan["launches"]
+        for ri, ((name, kpc_plan, wbytes), m) in enumerate(zip(plan["rows"], marks)):
+            names = [_short(e["kernel"]) for e in ds[m + 1:marks[ri + 1]]]
+            L = plan["launches"]
+
+            def periodic(p):
+                return 0 < L * p <= len(names) and all(names[j] == names[j % p] for j in range(L * p))
+            kpc = kpc_plan if periodic(kpc_plan) else next((p for p in range(1, len(names) // L + 1)
+                                                            if periodic(p)), None)
+            if kpc is None:
+                raise ValueError(f"{d}: row {name}: no {L} repeated calls after the marker")
+            if kpc != kpc_plan:
+                print(f"{d}: row {name}: {kpc} kernels per call (planned {kpc_plan})", file=sys.stderr)
+            seq = ds[m + 1:m + 1 + kpc * L]
             r = rows.setdefault(name, dict(weight_bytes=wbytes, kernels={}))
             for j in range(kpc):
                 calls = seq[j::kpc]
