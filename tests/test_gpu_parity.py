@@ -788,6 +788,16 @@ def test_moe_token_counts(q, oracle, T, topk):
     _moe_check(q, oracle, d, _moe_weights(oracle, d))
 
 
+@pytest.mark.parametrize("H", [2080, 4128, 8224, 16416])
+def test_moe_hidden_sizes(q, oracle, H):
+    """The fused first launch at every row length it serves (token rows of
+    2080, 4128 and 8224 values: 2, 4 and 8 chunks of 8 per thread) and the
+    separate quantiser and routing launches for longer rows (16416); each
+    stage as in the other FP8 MoE tests, the token quantisation bit-exact."""
+    d = gen.moe_config(E=4, H=H, I=32, T=5, topk=2, seed=75)
+    _moe_check(q, oracle, d, _moe_weights(oracle, d))
+
+
 @pytest.mark.parametrize("I", [32, 512, 1056, 2080])
 def test_moe_requant_row_lengths(q, oracle, I):
     """The fp32 intermediate's requantisation at every row-length path: a
