@@ -283,6 +283,25 @@ def test_gemm_w4a16_unaligned_steps(q, oracle):
         tol_check(g, y32, f"w4a16 unaligned steps M={M}")
 
 
+def test_gemm_w4a16_prefill_unaligned_steps(q, oracle):
+    """A prefill shape that the persistent W4A16 kernel serves (8 x 17 tiles
+    of 256, ragged M and N): that kernel loads the group steps as dwords, so
+    a step pointer 2 bytes past a 4-byte boundary takes the tiled kernel;
+    both alignments give the oracle's result."""
+    d = gen.linear_config(1, n=4112, k=128, m=2000)
+    ops = _operands(oracle, d, "w4a16")
+    y32, _ = _oracle_gemm(oracle, "w4a16", ops, 2000)
+    s = dev(ops["steps"])
+    buf = torch.empty(s.numel() + 8, dtype=s.dtype, device=s.device)
+    a, packed = dev(ops["a"]), dev(ops["packed"])
+    for off in (0, 1):  # bf16 elements past the (256-byte aligned) allocation
+        sv = buf[off:off + s.numel()].view(s.shape)
+        sv.copy_(s)
+        assert (sv.data_ptr() % 4 == 0) == (off == 0)
+        g = host(q.gemm_w4a16(a, packed, sv, out_dtype=torch.float32))
+        tol_check(g, y32, f"w4a16 prefill steps {2 * off} bytes past a 4-byte boundary")
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "int8", "w4a16"])
 def test_gemm_deterministic(q, oracle, fmt):
     """Bitwise-equal repeats, interleaved with calls of other shapes that
@@ -716,7 +735,7 @@ def test_lm_head_w4a16_full_table_sampled(q, oracle, vocab_full):
 # (N, K, M list): C2 decode layer; ragged K; a split-K grid (8 column tiles);
 # K past 16384 (the quantiser's two-pass rows); C3 layer
 LINEAR_CASES = [(8192, 2048, (1, 5, 8, 16)), (512, 80, (1, 3, 16)), (512, 2048, (1, 16)),
-                (1024, 16400, (2,)), (25600, 5120, (8,))]
+                (1024, 16400, (2,)), (25600, 5120, (1, 8, 16))]
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
