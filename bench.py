@@ -35,6 +35,8 @@ Counter tools (rocprofv3 runs of committed code):
                            markdown summaries kept under profiles/
   --summarize-trace CSV    group a rocprofv3 --kernel-trace CSV by kernel
                            and grid
+  --summarize-clock DIR ... shader clock per kernel (wave lifetime and
+                           GRBM_GUI_ACTIVE) from the counter runs above
 """
 
 from __future__ import annotations
@@ -89,6 +91,9 @@ def parse():
                     help="print the dispatches of a rocprofv3 --kernel-trace CSV grouped by kernel "
                          "and grid (count, average and minimum duration), largest total first")
     ap.add_argument("--trace-top", type=int, default=70, help="groups printed by --summarize-trace")
+    ap.add_argument("--summarize-clock", nargs="+", metavar="DIR", default=None,
+                    help="print the shader clock of each kernel (and grid) over its dispatches of at least "
+                         "20 us, bracketed by wave lifetime and GRBM_GUI_ACTIVE, from rocprofv3 --pmc runs")
     return ap.parse_args()
 
 
@@ -817,6 +822,36 @@ def _short(kernel):
     return k.replace("qlin::", "")
 
 
+def summarize_clock(dirs, min_us=20.0):
+    """Shader clock per kernel and grid, bracketed by two counter ratios
+    over dispatches of at least `min_us` (median per group):
+    * wave lifetime / duration (4 x SQ_WAVE_CYCLES / SQ_WAVES, quad-cycles,
+      over the dispatch time): a lower bound, close to the clock for kernels
+      whose waves all live the whole dispatch (one round of workgroups:
+      the decode GEMMs at these shapes, the persistent prefill kernels);
+    * GRBM_GUI_ACTIVE / 8 / duration: GPU clock cycles of each of the 8
+      XCDs (the counter summed over their instances, so a 3.3 ms
+      memory-bound kernel reads 2.31 GHz); the counter window is longer
+      than the kernel by about 16 k cycles per XCD (a 25 us repack reads
+      2.95 GHz against 2.33 at 128 us), an upper bound that is tight only
+      for long dispatches."""
+    import collections
+    import statistics
+
+    for d in dirs:
+        g = collections.defaultdict(list)
+        for e in _read_dispatches(d):
+            c = e["ctr"]
+            if "GRBM_GUI_ACTIVE" in c and c.get("SQ_WAVES") and e["ns"] >= min_us * 1e3:
+                life = 4.0 * c["SQ_WAVE_CYCLES"] / c["SQ_WAVES"]
+                g[(_short(e["kernel"]), e["grid"])].append((e["ns"], life / e["ns"], c["GRBM_GUI_ACTIVE"] / e["ns"] / 8))
+        print(f"{d}: kernel, grid (work-items), dispatches, median us, GHz from wave lifetime (lower "
+              f"bound), GHz from GRBM_GUI_ACTIVE (upper bound)")
+        for (k, grid), v in sorted(g.items(), key=lambda kv: -statistics.median(x[0] for x in kv[1])):
+            print(f"  {k[:64]:64s} {grid:>9s} {len(v):4d} {statistics.median(x[0] for x in v) / 1e3:9.1f} "
+                  f"{statistics.median(x[1] for x in v):6.2f} {statistics.median(x[2] for x in v):6.2f}")
+
+
 def summarize_trace(csv_path, top):
     """Group the dispatches of a kernel-trace CSV by kernel (name without
     namespace and argument list) and grid in workgroups; one line per group,
@@ -1131,6 +1166,9 @@ def main():
         return
     if a.summarize_trace:
         summarize_trace(a.summarize_trace, a.trace_top)
+        return
+    if a.summarize_clock:
+        summarize_clock(a.summarize_clock)
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this build measures the "
