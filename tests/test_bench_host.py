@@ -97,3 +97,34 @@ def test_pmc_summary_rejects_short_rows(bench, tmp_path):
                    "sources_sha256": "0" * 64}, fh)
     with pytest.raises(ValueError):
         bench.summarize_pmc([d1], str(tmp_path / "x.md"), [])
+
+
+def test_clock_summary_bounds(bench, tmp_path, capsys):
+    """--summarize-clock: per kernel and grid, the wave-lifetime clock (4 x
+    SQ_WAVE_CYCLES / SQ_WAVES over the dispatch time) and the GRBM clock
+    (GRBM_GUI_ACTIVE / 8 XCDs over it), medians over dispatches of at least
+    20 us; shorter dispatches are left out."""
+    import csv
+    d = tmp_path / "clk"
+    d.mkdir()
+    rows = []
+    # kernel a: 3 dispatches of 100 us; waves live 2.0 GHz x 100 us, GRBM 2.2 GHz x 8 XCDs
+    for i, ns in enumerate((100_000, 100_000, 100_000), 1):
+        rows.append((i, "void qlin::a(int)", ns, dict(SQ_WAVES=10.0, SQ_WAVE_CYCLES=10 * 2.0 * ns / 4,
+                                                       GRBM_GUI_ACTIVE=8 * 2.2 * ns)))
+    # kernel b: one 10 us dispatch (too short, left out)
+    rows.append((4, "void qlin::b(int)", 10_000, dict(SQ_WAVES=4.0, SQ_WAVE_CYCLES=4 * 2.0 * 10_000 / 4,
+                                                       GRBM_GUI_ACTIVE=8 * 3.0 * 10_000)))
+    with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "VGPR_Count",
+                    "LDS_Block_Size", "Start_Timestamp", "End_Timestamp", "Counter_Name", "Counter_Value"])
+        for i, k, ns, ctr in rows:
+            for n, v in ctr.items():
+                w.writerow([i, k, 256, 256, 32, 0, 1000, 1000 + ns, n, v])
+    bench.summarize_clock([str(d)])
+    out = capsys.readouterr().out.splitlines()
+    lines = [l.split() for l in out[1:]]
+    assert len(lines) == 1 and lines[0][0] == "a"
+    n, us, lo, hi = int(lines[0][2]), float(lines[0][3]), float(lines[0][4]), float(lines[0][5])
+    assert n == 3 and us == 100.0 and lo == 2.0 and hi == 2.2
